@@ -1,0 +1,257 @@
+"""Float64 CPU oracle for the quantized-softmax attention forward.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+GPU path is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.  It
+shares no code, constant or table with the HIP library.
+
+What it computes, per (batch b, query head h), for query rows i and keys j:
+
+    s_ij = scale * q_i . k_j                       (scale = 1/sqrt(d) by default)
+    O_i  = sum_j w_ij v_j / sum_j w_ij             (w: the weight function)
+
+with three kinds of weight function w(s) replacing exp(s - m):
+
+* ``exact``  -- w = exp(s - m_i), i.e. ordinary softmax attention, the
+  control that the approximate forms replace (both pages note that softmax
+  usually stays at higher precision than the attention matmuls).
+* ``kint``   -- K-interval attention ("Pretraining Transformers with Quantized
+  Softmax in Attention", abstract and chapters 1, 5, 6): the exponential is
+  read off K+1 grid values fitted to each row of scores.  The grid spans the
+  row's calibration range [lo_i, m_i]: min-max calibration takes lo_i = the
+  row minimum, fixed-window calibration takes lo_i = m_i - W.  Grid points are
+  g_l = m_i - l*Delta_i with Delta_i = (m_i - lo_i)/K, l = 0..K, and grid
+  values T_l = exp(-l*Delta_i).  With y = (m_i - s)/Delta_i, hard rounding
+  takes w = T_rint(y); interpolation takes the straight line between the two
+  neighbouring grid values.
+* ``pot``    -- Rowmax-PoT ("Approximating Softmax in Pretrained LLMs: Model
+  Sensitivity and Kernel Acceleration", abstract; the wiki page's flowchart
+  "Row max -> Power-of-two weights"): a coarse logarithmic weight anchored at
+  the row maximum.  With y = (m_i - s) * log2(e), e = rint(y) clipped to the
+  stated level count L, w = 2**-e.
+
+Readings taken where the pages are silent (every one is listed in the design
+notes of the repository with its reason):
+  R1  the grid lives in the score domain and is uniformly spaced;
+  R2  K counts intervals, so there are K+1 grid values, both ends included;
+  R4  fixed window: scores below m - W saturate to T_K, or give 0 with flush;
+  R5  PoT: e saturates at L-1 (L distinct weights), or e >= L gives 0 with
+      flush;
+  R6  rint is round-half-to-even;
+  R7  the index is measured from the anchor m_i (l = rint((m - s)/Delta));
+  R8  interpolation is linear in the weight (exp) domain;
+  R9  a min-max row whose visible scores are all equal has Delta = 0: every
+      visible weight is 1;
+  R10 extrema are taken over the keys visible to the row (causal: j <= i,
+      top-left aligned);
+  R11 normalisation divides by the sum of the approximate weights;
+  R15 query head h reads KV head floor(h / (H/Hkv)).
+
+Index code per element (what the GPU may dump for parity): the grid index
+l (kint) or exponent e (pot), clipped as the weight was; 254 for a flushed
+element, 255 for a masked (invisible) one; exact kinds store 0.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+LOG2E = 1.0 / math.log(2.0)
+IDX_FLUSHED = 254
+IDX_MASKED = 255
+
+
+# ---------------------------------------------------------------------------
+# Decoding of the stored formats (exact; each value maps to one real number)
+# ---------------------------------------------------------------------------
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64.  A bfloat16 is the upper
+    half of an IEEE binary32, so widening the pattern is exact."""
+    b32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b32.view(np.float32).astype(np.float64)
+
+
+def decode_f32(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 (``fn``: finite, no infinities) bit patterns -> float64.
+
+    1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent field 0
+    is subnormal: m/8 * 2**-6.  The pattern S.1111.111 is NaN; every other
+    pattern is finite, up to 448 = 1.75 * 2**8.
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    ex = (b >> 3) & 0xF
+    man = (b & 0x7).astype(np.float64)
+    val = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    val = np.where((ex == 0xF) & ((b & 0x7) == 0x7), np.nan, val)
+    return sign * val
+
+
+# ---------------------------------------------------------------------------
+# The weight functions (one row chunk at a time)
+# ---------------------------------------------------------------------------
+
+def _check_kind(kind, levels, window, interp, flush):
+    if kind not in ("exact", "kint", "pot"):
+        raise ValueError(f"unknown kind {kind!r}")
+    if kind == "kint" and not (isinstance(levels, int) and levels >= 1):
+        raise ValueError("kint needs levels = K >= 1 intervals")
+    if kind == "pot" and not (isinstance(levels, int) and levels >= 1):
+        raise ValueError("pot needs levels = L >= 1")
+    if window is not None and not (window > 0 and math.isfinite(window)):
+        raise ValueError("window must be finite and > 0")
+    if interp and kind != "kint":
+        raise ValueError("interpolation is a K-interval option")
+    if window is not None and kind != "kint":
+        raise ValueError("fixed-window calibration is a K-interval option")
+    if flush and kind == "exact":
+        raise ValueError("flush applies to kint and pot")
+
+
+def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Optional[int] = None,
+                window: Optional[float] = None, interp: bool = False, flush: bool = False):
+    """Weights for a block of score rows.
+
+    S: (R, N) float64 scaled scores; visible: (R, N) bool, at least one True
+    per row.  Returns dict with w (R,N), idx (R,N) uint8, y (R,N) grid
+    coordinate (nan where masked; for exact kinds y = m - s), m, lo, delta (R,)
+    and the table T (R, K+1) for kint.
+    """
+    _check_kind(kind, levels, window, interp, flush)
+    R, N = S.shape
+    neg = np.where(visible, S, -np.inf)
+    pos = np.where(visible, S, np.inf)
+    m = neg.max(axis=1)                                   # row max over visible keys (anchor)
+    mn = pos.min(axis=1)                                  # row min over visible keys
+    out = {"m": m}
+    idx = np.full((R, N), IDX_MASKED, dtype=np.uint8)
+
+    if kind == "exact":
+        y = np.where(visible, m[:, None] - S, np.nan)
+        w = np.where(visible, np.exp(np.where(visible, S - m[:, None], 0.0)), 0.0)
+        idx[visible] = 0
+        out.update(w=w, idx=idx, y=y, lo=mn, delta=np.zeros(R))
+        return out
+
+    if kind == "pot":
+        L = levels
+        y = np.where(visible, (m[:, None] - S) * LOG2E, np.nan)
+        e = np.rint(np.where(visible, y, 0.0))            # round half to even
+        if flush:
+            kept = visible & (e <= L - 1)
+            flushed = visible & ~kept
+        else:
+            e = np.minimum(e, L - 1)
+            kept = visible
+            flushed = np.zeros_like(visible)
+        w = np.where(kept, np.exp2(-np.where(kept, e, 0.0)), 0.0)
+        idx[kept] = e[kept].astype(np.uint8)
+        idx[flushed] = IDX_FLUSHED
+        out.update(w=w, idx=idx, y=y, lo=mn, delta=np.full(R, 1.0 / LOG2E))
+        return out
+
+    # K-interval
+    K = levels
+    lo = (m - window) if window is not None else mn
+    delta = (m - lo) / K
+    ell = np.arange(K + 1, dtype=np.float64)
+    T = np.exp(-ell[None, :] * delta[:, None])            # K+1 grid values per row, T_0 = 1
+    degenerate = delta == 0.0                             # min-max row with all scores equal
+    safe = np.where(degenerate, 1.0, delta)
+    y = np.where(visible, (m[:, None] - S) / safe[:, None], np.nan)
+    y = np.where(degenerate[:, None] & visible, 0.0, y)
+    yv = np.where(visible, y, 0.0)
+    rows = np.arange(R)[:, None]
+    if not interp:
+        l = np.rint(yv)                                   # nearest grid point, half to even
+        if flush:
+            kept = visible & (yv <= K)                    # below the window -> flushed
+        else:
+            kept = visible
+        l = np.minimum(l, K)
+        li = l.astype(np.int64)
+        w = np.where(kept, T[rows, li], 0.0)
+    else:
+        if flush:
+            kept = visible & (yv <= K)
+        else:
+            kept = visible
+        yc = np.minimum(yv, float(K))
+        l0 = np.minimum(np.floor(yc), K - 1).astype(np.int64)   # left grid point
+        t = yc - l0
+        w_lin = (1.0 - t) * T[rows, l0] + t * T[rows, l0 + 1]
+        w = np.where(kept, w_lin, 0.0)
+        li = np.minimum(np.floor(yc), K).astype(np.int64)
+    flushed = visible & ~kept
+    idx[kept] = li[kept].astype(np.uint8)
+    idx[flushed] = IDX_FLUSHED
+    out.update(w=w, idx=idx, y=y, lo=lo, delta=delta, T=T)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Attention forward
+# ---------------------------------------------------------------------------
+
+def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Sequence[int]] = None, *,
+              causal: bool = False, kind: str = "exact", levels: Optional[int] = None,
+              window: Optional[float] = None, interp: bool = False, flush: bool = False,
+              scale: Optional[float] = None, detail: bool = False, chunk: int = 512):
+    """One (batch, head) pair: qh (N, d), kh/vh (N, d) float64.
+
+    ``rows`` selects query rows (default: all).  Returns dict with O (R, d),
+    m, lo, l (R,) and, if ``detail``, w, idx, y (R, N) and delta (R,).
+    """
+    Nq, d = qh.shape
+    N = kh.shape[0]                                        # keys (equal to Nq in attention proper)
+    sc = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    parts = {}
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        S = sc * (qh[r] @ kh.T)                            # scaled scores, float64
+        cols = np.arange(N)
+        visible = (cols[None, :] <= r[:, None]) if causal else np.ones((len(r), N), dtype=bool)
+        rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush)
+        w = rw["w"]
+        l = w.sum(axis=1)                                  # row sum of the approximate weights
+        O = (w @ vh) / l[:, None]                          # normalise, then P.V
+        piece = {"O": O, "m": rw["m"], "lo": rw["lo"], "l": l}
+        if detail:
+            piece.update(w=w, idx=rw["idx"], y=rw["y"], delta=rw["delta"])
+        for key, val in piece.items():
+            parts.setdefault(key, []).append(val)
+    return {key: np.concatenate(val, axis=0) for key, val in parts.items()}
+
+
+def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = False, kind: str = "exact",
+             levels: Optional[int] = None, window: Optional[float] = None, interp: bool = False,
+             flush: bool = False, scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+             detail: bool = False):
+    """Attention forward over all heads.
+
+    q: (B, H, N, d); k, v: (B, Hkv, N, d), float64 (already decoded from the
+    stored format and multiplied by any per-tensor descale).  Returns dict of
+    arrays with leading (B, H) axes.
+    """
+    B, H, Nq, d = q.shape
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    group = H // Hkv
+    res = {}
+    for b in range(B):
+        for h in range(H):
+            kv = h // group                                # query head h reads KV head floor(h/group)
+            r = head_rows(q[b, h], k[b, kv], v[b, kv], rows, causal=causal, kind=kind, levels=levels,
+                          window=window, interp=interp, flush=flush, scale=scale, detail=detail)
+            for key, val in r.items():
+                res.setdefault(key, []).append(val)
+    return {key: np.stack(val).reshape((B, H) + val[0].shape) for key, val in res.items()}

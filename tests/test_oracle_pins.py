@@ -1,0 +1,371 @@
+"""Pins for the float64 oracle: things the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula.  They check it against
+hand-worked examples (tests/golden), a library routine (PyTorch's SDPA in
+float64), closed-form error bounds, invariants, special cases, and an
+independent scalar brute-force implementation.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import scalar
+from quantized_softmax_approximation_amd import inputs as qin
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+LN2 = math.log(2.0)
+
+
+def _ev(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"exp": math.exp, "log": math.log}))
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _rand_qkv(B=1, H=2, Hkv=None, N=24, d=16, sigma=1.0, seed=0):
+    r = _rng(seed)
+    Hkv = H if Hkv is None else Hkv
+    q = r.standard_normal((B, H, N, d)) * sigma
+    k = r.standard_normal((B, Hkv, N, d)) * sigma
+    v = r.standard_normal((B, Hkv, N, d))
+    return q, k, v
+
+
+VARIANTS = [
+    dict(kind="exact"),
+    dict(kind="pot", levels=8),
+    dict(kind="pot", levels=4, flush=True),
+    dict(kind="pot", levels=1),
+    dict(kind="kint", levels=4),
+    dict(kind="kint", levels=16),
+    dict(kind="kint", levels=4, interp=True),
+    dict(kind="kint", levels=4, window=8.0),
+    dict(kind="kint", levels=4, window=3.0, flush=True),
+    dict(kind="kint", levels=16, window=8.0, interp=True),
+    dict(kind="kint", levels=4, window=3.0, interp=True, flush=True),
+]
+
+
+# --------------------------------------------------------------------------- golden
+
+def test_golden_rows():
+    g = json.load(open(GOLDEN))
+    for ex in g["rows"]:
+        S = np.array([[_ev(s) for s in ex["scores"]]])
+        vis = np.ones_like(S, dtype=bool)
+        rw = oracle.row_weights(S, vis, kind=ex["kind"], levels=ex["levels"], window=ex.get("window"),
+                                interp=ex.get("interp", False), flush=ex.get("flush", False))
+        want = np.array([_ev(w) for w in ex["weights"]])
+        np.testing.assert_allclose(rw["w"][0], want, rtol=1e-14, atol=0, err_msg=ex["name"])
+        assert rw["idx"][0].tolist() == ex["index"], ex["name"]
+        # the scalar implementation agrees on every hand example too
+        ws = scalar.weight_row(S[0].tolist(), [True] * S.shape[1], ex["kind"], ex["levels"], ex.get("window"),
+                               ex.get("interp", False), ex.get("flush", False))
+        np.testing.assert_allclose(ws, want, rtol=1e-14, atol=0, err_msg=ex["name"])
+
+
+def test_golden_attention_exact_rationals():
+    g = json.load(open(GOLDEN))
+    for ex in g["attention"]:
+        q = np.array(ex["q"])[None, None]
+        k = np.array(ex["k"])[None, None]
+        v = np.array(ex["v"])[None, None]
+        r = oracle.attn_fwd(q, k, v, kind=ex["kind"], levels=ex["levels"], flush=ex["flush"], scale=ex["scale"])
+        want = [Fraction(x) for x in ex["O"]]
+        np.testing.assert_allclose(r["O"][0, 0, 0], [float(x) for x in want], rtol=1e-15)
+        rs = scalar.attention(ex["q"], ex["k"], ex["v"], kind=ex["kind"], levels=ex["levels"],
+                              flush=ex["flush"], scale=ex["scale"], exact_pot=True)
+        assert rs[0] == want, ex["name"]
+
+
+# --------------------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 2), (6, 1)])
+def test_exact_equals_sdpa_float64(causal, H, Hkv):
+    q, k, v = _rand_qkv(B=2, H=H, Hkv=Hkv, N=33, d=16, sigma=1.3, seed=11)
+    r = oracle.attn_fwd(q, k, v, causal=causal, kind="exact")
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal,
+        enable_gqa=(H != Hkv)).numpy()
+    np.testing.assert_allclose(r["O"], ref, rtol=0, atol=1e-12)
+
+
+def test_exact_equals_sdpa_with_scale():
+    q, k, v = _rand_qkv(N=20, d=8, seed=3)
+    r = oracle.attn_fwd(q, k, v, kind="exact", scale=0.37)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.37).numpy()
+    np.testing.assert_allclose(r["O"], ref, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- per-row invariants
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+@pytest.mark.parametrize("causal", [False, True])
+def test_anchor_weight_one_and_rows_normalise(var, causal):
+    q, k, v = _rand_qkv(N=40, d=16, sigma=1.5, seed=5)
+    r = oracle.attn_fwd(q, k, v, causal=causal, detail=True, **var)
+    w, idx = r["w"], r["idx"]
+    N = q.shape[2]
+    vis = np.tril(np.ones((N, N), bool)) if causal else np.ones((N, N), bool)
+    S = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(q.shape[-1])
+    Sm = np.where(vis, S, -np.inf)
+    jmax = Sm.argmax(-1)
+    wmax = np.take_along_axis(w, jmax[..., None], -1)[..., 0]
+    assert np.all(wmax == 1.0)                              # the row max gets weight exactly 1
+    P = w / w.sum(-1, keepdims=True)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-12)  # rows normalise to 1
+    assert np.all(w[..., ~vis] == 0) and np.all(idx[..., ~vis] == 255)
+    np.testing.assert_allclose(r["m"], Sm.max(-1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 16])
+@pytest.mark.parametrize("window", [None, 2.0, 8.0])
+def test_kint_hard_at_most_K_plus_1_values_on_grid(K, window):
+    q, k, v = _rand_qkv(N=64, d=16, sigma=1.5, seed=K)
+    r = oracle.attn_fwd(q, k, v, kind="kint", levels=K, window=window, detail=True)
+    w, delta = r["w"], r["delta"]
+    for b, h, i in np.ndindex(w.shape[:3]):
+        vals = np.unique(w[b, h, i])
+        assert len(vals) <= K + 1
+        grid = np.exp(-np.arange(K + 1) * delta[b, h, i])  # membership: each weight is e^{-l Delta}
+        assert np.all(np.min(np.abs(vals[:, None] - grid[None, :]), axis=1) <= 1e-15)
+
+
+@pytest.mark.parametrize("L", [1, 2, 8, 16])
+@pytest.mark.parametrize("flush", [False, True])
+def test_pot_weights_are_exact_powers_of_two(L, flush):
+    q, k, v = _rand_qkv(N=64, d=16, sigma=2.0, seed=L)
+    r = oracle.attn_fwd(q, k, v, kind="pot", levels=L, flush=flush, detail=True)
+    w, idx = r["w"], r["idx"]
+    nz = w[w > 0]
+    mant, ex = np.frexp(nz)
+    assert np.all(mant == 0.5)                               # bit-exact 2^-e
+    e = 1 - ex
+    assert e.min() >= 0 and e.max() <= L - 1
+    for b, h, i in np.ndindex(w.shape[:3]):
+        assert len(np.unique(w[b, h, i])) <= L + (1 if flush else 0)
+    kept = (idx != 254) & (idx != 255)
+    np.testing.assert_array_equal(w[kept], np.exp2(-idx[kept].astype(float)))
+
+
+# --------------------------------------------------------------------------- closed-form error bounds
+
+def _ratio_bounds(q, k, v, **var):
+    r = oracle.attn_fwd(q, k, v, detail=True, **var)
+    ex = oracle.attn_fwd(q, k, v, kind="exact", detail=True)
+    P = r["w"] / r["w"].sum(-1, keepdims=True)
+    Pe = ex["w"] / ex["w"].sum(-1, keepdims=True)
+    return P / Pe, r
+
+
+@pytest.mark.parametrize("K", [2, 4, 16])
+def test_kint_hard_bound(K):
+    q, k, v = _rand_qkv(N=48, d=16, sigma=1.5, seed=21)
+    ratio, r = _ratio_bounds(q, k, v, kind="kint", levels=K)
+    D = r["delta"][..., None]
+    assert np.all(ratio <= np.exp(D) * (1 + 1e-12)) and np.all(ratio >= np.exp(-D) * (1 - 1e-12))
+    # the per-element weight error is at most half a step in the log domain
+    S = np.einsum("bhid,bhjd->bhij", q, k) / 4.0
+    lw = np.log(r["w"]) - (S - r["m"][..., None])
+    assert np.all(np.abs(lw) <= D / 2 + 1e-12)
+
+
+@pytest.mark.parametrize("K", [2, 4, 16])
+def test_kint_interp_bound_and_convexity(K):
+    q, k, v = _rand_qkv(N=48, d=16, sigma=1.5, seed=22)
+    ratio, r = _ratio_bounds(q, k, v, kind="kint", levels=K, interp=True)
+    D = r["delta"][..., None]
+    assert np.all(ratio <= np.exp(D ** 2 / 8) * (1 + 1e-12))
+    assert np.all(ratio >= np.exp(-D ** 2 / 8) * (1 - 1e-12))
+    S = np.einsum("bhid,bhjd->bhij", q, k) / 4.0
+    w_exact = np.exp(S - r["m"][..., None])
+    assert np.all(r["w"] >= w_exact * (1 - 1e-13))          # chord of a convex function lies above it
+    lw = np.log(r["w"]) - np.log(w_exact)
+    assert np.all(lw <= D ** 2 / 8 + 1e-12)
+
+
+def test_pot_bound():
+    q, k, v = _rand_qkv(N=48, d=16, sigma=2.0, seed=23)
+    ratio, r = _ratio_bounds(q, k, v, kind="pot", levels=64)   # L large: no saturation
+    assert np.all(ratio <= 2.0 * (1 + 1e-12)) and np.all(ratio >= 0.5 * (1 - 1e-12))
+
+
+def test_kint_converges_to_exact_softmax():
+    q, k, v = _rand_qkv(N=48, d=16, sigma=1.5, seed=24)
+    ex = oracle.attn_fwd(q, k, v, kind="exact")
+    errs = []
+    for K in (4, 16, 64, 256, 1024):
+        for interp in (False, True):
+            r = oracle.attn_fwd(q, k, v, kind="kint", levels=K, interp=interp)
+            errs.append((K, interp, np.max(np.abs(r["O"] - ex["O"]))))
+    hard = [e for (K, i, e) in errs if not i]
+    lin = [e for (K, i, e) in errs if i]
+    # hard rounding converges linearly in 1/K, interpolation quadratically (error ~ Delta^2/8)
+    assert all(a > 2 * b for a, b in zip(hard, hard[1:])) and hard[-1] < 5e-3
+    assert all(a > 8 * b for a, b in zip(lin, lin[1:])) and lin[-1] < 1e-4
+
+
+# --------------------------------------------------------------------------- special cases
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+def test_single_visible_key_and_uniform_scores(var):
+    q, k, v = _rand_qkv(N=16, d=8, seed=31)
+    r = oracle.attn_fwd(q, k, v, causal=True, **var)
+    np.testing.assert_allclose(r["O"][:, :, 0], v[:, :, 0], atol=1e-15)   # causal row 0 sees key 0 only
+    r0 = oracle.attn_fwd(np.zeros_like(q), k, v, causal=False, **var)      # all scores 0
+    np.testing.assert_allclose(r0["O"], np.broadcast_to(v.mean(2, keepdims=True), v.shape), atol=1e-14)
+
+
+def test_pot_one_level_is_uniform_weighting():
+    q, k, v = _rand_qkv(N=16, d=8, sigma=2.0, seed=32)
+    r = oracle.attn_fwd(q, k, v, kind="pot", levels=1, causal=True)
+    csum = np.cumsum(v, axis=2) / np.arange(1, 17)[None, None, :, None]
+    np.testing.assert_allclose(r["O"], csum, atol=1e-14)
+
+
+def test_kint_K1_minmax_splits_at_midpoint():
+    q, k, v = _rand_qkv(N=32, d=8, sigma=1.5, seed=33)
+    r = oracle.attn_fwd(q, k, v, kind="kint", levels=1, detail=True)
+    S = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(8)
+    m, mn = S.max(-1, keepdims=True), S.min(-1, keepdims=True)
+    want = np.where(S > (m + mn) / 2, 1.0, np.exp(mn - m))
+    np.testing.assert_allclose(r["w"], want, rtol=1e-14)
+
+
+@pytest.mark.parametrize("interp", [False, True])
+def test_grid_exact_scores_equal_exact_softmax(interp):
+    # d = 1, scale 1: scores are the keys; put every score on a grid point m - n*Delta
+    K, step = 8, 0.375
+    n = np.array([0, 3, 8, 1, 5, 8, 2, 0, 7, 4])
+    kk = (-n * step)[None, None, :, None]
+    qq = np.ones((1, 1, 3, 1))
+    vv = _rng(4).standard_normal((1, 1, len(n), 3))
+    for kw in (dict(window=None), dict(window=K * step)):
+        r = oracle.attn_fwd(qq, kk, vv, kind="kint", levels=K, interp=interp, scale=1.0, **kw)
+        ex = oracle.attn_fwd(qq, kk, vv, kind="exact", scale=1.0)
+        np.testing.assert_allclose(r["O"][..., :1, :], ex["O"][..., :1, :], rtol=1e-14)
+
+
+# --------------------------------------------------------------------------- equivalences and symmetry
+
+@pytest.mark.parametrize("L", [2, 4, 8, 16])
+def test_pot_is_kint_window_special_case(L):
+    # PoT(L) = K-interval hard with K = L-1 intervals over the window W = (L-1) ln 2
+    q, k, v = _rand_qkv(N=64, d=16, sigma=2.0, seed=40 + L)
+    pot = oracle.attn_fwd(q, k, v, kind="pot", levels=L, detail=True)
+    kin = oracle.attn_fwd(q, k, v, kind="kint", levels=L - 1, window=(L - 1) * LN2, detail=True)
+    frac = np.abs(pot["y"] - np.floor(pot["y"]) - 0.5)
+    away = frac > 1e-9                                       # away from rounding ties
+    assert away.mean() > 0.999
+    np.testing.assert_array_equal(pot["idx"][away], kin["idx"][away])
+    np.testing.assert_allclose(pot["w"][away], kin["w"][away], rtol=1e-13)
+
+
+@pytest.mark.parametrize("var", VARIANTS[:6], ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+def test_shift_and_scale_invariance(var):
+    r = _rng(50)
+    S = np.round(r.standard_normal((6, 30)) * 8) / 8.0            # dyadic scores: shifts are exact
+    vis = np.ones_like(S, dtype=bool)
+    a = oracle.row_weights(S, vis, **var)
+    b = oracle.row_weights(S + 0.625, vis, **var)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    np.testing.assert_allclose(a["w"], b["w"], rtol=1e-14)
+    if var["kind"] == "kint" and var.get("window") is None:
+        c = oracle.row_weights(S * 4.0, vis, **var)                # min-max grid scales with the row
+        np.testing.assert_array_equal(a["idx"], c["idx"])
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+def test_key_permutation_and_gqa(var):
+    q, k, v = _rand_qkv(B=1, H=4, Hkv=2, N=20, d=8, sigma=1.5, seed=60)
+    r = oracle.attn_fwd(q, k, v, **var)
+    perm = _rng(61).permutation(20)
+    rp = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm], **var)
+    np.testing.assert_allclose(r["O"], rp["O"], atol=1e-13)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    rm = oracle.attn_fwd(q, kr, vr, **var)
+    np.testing.assert_array_equal(r["O"], rm["O"])
+    # heads are independent: head 3 alone equals head 3 of the batch
+    r3 = oracle.attn_fwd(q[:, 3:4], k[:, 1:2], v[:, 1:2], **var)
+    np.testing.assert_array_equal(r3["O"][:, 0], r["O"][:, 3])
+
+
+def test_row_subset_matches_full():
+    q, k, v = _rand_qkv(N=40, d=8, seed=70)
+    for var in VARIANTS:
+        full = oracle.attn_fwd(q, k, v, causal=True, **var)
+        rows = [0, 7, 39, 13]
+        sub = oracle.attn_fwd(q, k, v, causal=True, rows=rows, **var)
+        np.testing.assert_array_equal(sub["O"], full["O"][:, :, rows])
+
+
+# --------------------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_scalar_agrees(var, causal):
+    for seed in range(6):
+        n = 3 + seed % 6
+        q, k, v = _rand_qkv(B=1, H=1, N=n, d=4, sigma=1.7, seed=100 + seed)
+        r = oracle.attn_fwd(q, k, v, causal=causal, **var)
+        rs = scalar.attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal=causal, **var)
+        np.testing.assert_allclose(r["O"][0, 0], np.array(rs, dtype=float), atol=1e-13)
+
+
+def test_brute_force_pot_exact_rational():
+    for seed in range(5):
+        q, k, v = _rand_qkv(B=1, H=1, N=4, d=4, sigma=2.0, seed=200 + seed)
+        v = np.round(v * 16) / 16                                     # dyadic V: O is an exact rational
+        r = oracle.attn_fwd(q, k, v, kind="pot", levels=4)
+        rs = scalar.attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), kind="pot", levels=4,
+                              exact_pot=True)
+        for i in range(4):
+            for c in range(4):
+                assert abs(Fraction(r["O"][0, 0, i, c]) - rs[i][c]) <= abs(rs[i][c]) * Fraction(1, 2 ** 50)
+
+
+# --------------------------------------------------------------------------- decoding of stored formats
+
+def test_decode_e4m3fn_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_decode_bf16_matches_torch():
+    x = torch.randn(4096, dtype=torch.float32).to(torch.bfloat16)
+    ours = oracle.decode_bf16(qin.raw_bits(x))
+    np.testing.assert_array_equal(ours, x.to(torch.float64).numpy())
+
+
+def test_workload_inputs_have_stated_logit_std():
+    wl = qin.custom(B=1, H=2, N=512, d=128, dtype="bf16", sigma_qk=1.5, seed=9)
+    x = qin.make_inputs(wl)
+    q = oracle.decode_bf16(qin.raw_bits(x.q)).reshape(x.q.shape)
+    k = oracle.decode_bf16(qin.raw_bits(x.k)).reshape(x.k.shape)
+    s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(128)
+    assert abs(s.std() - 2.25) < 0.1
+
+
+def test_sink_workload_boosts_key0_by_six():
+    wl = qin.WORKLOADS["pot2k"].replace(B=1, H=2, Hkv=2, N=256)
+    x = qin.make_inputs(wl)
+    q = oracle.decode_bf16(qin.raw_bits(x.q)).reshape(x.q.shape)
+    k = oracle.decode_bf16(qin.raw_bits(x.k)).reshape(x.k.shape)
+    s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(128)
+    # key 0's score sits about 6 above the others' mean in every row
+    assert abs((s[..., 0].mean() - s[..., 1:].mean()) - 6.0) < 0.5
