@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-softmax attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload fp8_8k] [--dtype fp8|bf16]
+                    [--kind pot --levels 16] [--causal] [--no-cpu-baseline] [--no-variants]
+
+A step is one call of the whole fused forward (row-extrema pre-pass, score
+tiles, weight formation, PV, epilogue) over the workload's full batch, with
+inputs resident in HBM.  The headline workload is fp8 e4m3 Q/K/V at N = 8192
+(B = 1, H = 32, d = 128, non-causal), Rowmax-PoT with 16 levels.
+
+Prints ONE JSON line: the throughput in credited TFLOP/s (4 d flops per
+visible query-key pair, the same for every variant), the roofline of the
+kernel (MFMA flops the algorithm needs per launch / measured launch time),
+a table of the other variants on the same inputs (median, p10, p90 of
+per-call HIP-event times) and the float64 oracle's rate on a bounded sample
+of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_softmax_approximation_amd as qsa  # noqa: E402
+from quantized_softmax_approximation_amd import inputs as qin  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s + % MFMA peak at N=8K (PoT vs exact exp)"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}   # MI355X dense MFMA / fp32 vector
+DT_NAME = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3", torch.float32: "f32"}
+
+
+def pairs(B, H, N, causal):
+    return B * H * (N * (N + 1) // 2 if causal else N * N)
+
+
+def mfma_flops_per_pair(kind, d):
+    """MFMA work the algorithm needs per visible pair: QK^T and PV (2d each),
+    plus one more QK^T for the row-extrema pre-pass of anchored kinds."""
+    return 4 * d if kind == "exact" else 6 * d
+
+
+def src_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_softmax_approximation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def call(dev_t, x, var, causal, out):
+    q, k, v = dev_t
+    fp8 = q.dtype == torch.float8_e4m3fn
+    return qsa.attn_fwd_ex(q, k, v, causal=causal, out=out, q_descale=x.q_descale if fp8 else 0.0,
+                           k_descale=x.k_descale if fp8 else 0.0, v_descale=x.v_descale if fp8 else 0.0, **var)
+
+
+def time_loop(fn, steps, warmup):
+    """Mean launch time over `steps` back-to-back calls, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_calls(fn, n, warmup=5):
+    """Per-call HIP-event times (ms) and host-side call latency (call + sync)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    host = []
+    for _ in range(min(n, 20)):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - t0) * 1e3)
+    return t, float(np.median(host))
+
+
+def cpu_baseline(x, var, causal, budget_s):
+    """The float64 oracle on a bounded sample (chunks of 512 query rows of
+    successive heads until `budget_s` seconds), scaled to credited TFLOP/s."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    B, H, N, d = x.q.shape
+    group = H // x.k.shape[1]
+    t0 = time.perf_counter()
+    done_pairs = 0
+    rows_done = 0
+    heads = 0
+    okind = dict(var)
+    if okind["kind"] == "exact_anchored":
+        okind["kind"] = "exact"
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        dec = []
+        for t, s, hh in ((x.q, x.q_descale, h), (x.k, x.k_descale, h // group), (x.v, x.v_descale, h // group)):
+            bits = qin.raw_bits(t[b, hh])
+            f = (oracle.decode_e4m3fn(bits) * s if t.dtype == torch.float8_e4m3fn else
+                 oracle.decode_bf16(bits) if t.dtype == torch.bfloat16 else oracle.decode_f32(bits))
+            dec.append(f.reshape(N, d))
+        heads += 1
+        for r0 in range(0, N, 512):
+            rows = np.arange(r0, min(N, r0 + 512))
+            oracle.head_rows(*dec, rows, causal=causal, **okind)
+            rows_done += len(rows)
+            done_pairs += int(np.sum(rows + 1)) if causal else len(rows) * N
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(4 * d * done_pairs / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows_done} query rows x {N} keys over {heads} head(s) of the same workload, "
+                      f"{el:.1f} s, float64 NumPy; rate scaled to credited TFLOP/s (4 d flops per visible pair)"}
+
+
+def traffic_for(workload, dtype, var, causal, per_launch_flops):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        recs = json.load(open(path))
+    except ValueError:
+        return None
+    key = f"{workload}:{dtype}:{var['kind']}{var.get('levels', '')}:{'causal' if causal else 'noncausal'}"
+    r = recs.get(key)
+    if not r or r.get("src_hash") != src_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp8_8k", choices=sorted(qin.WORKLOADS))
+    ap.add_argument("--dtype", default=None, choices=["fp8", "bf16", "f32"])
+    ap.add_argument("--kind", default="pot", choices=["pot", "exact", "exact_anchored", "kint"])
+    ap.add_argument("--levels", type=int, default=16)
+    ap.add_argument("--window", type=float, default=None)
+    ap.add_argument("--interp", action="store_true")
+    ap.add_argument("--causal", action="store_true", help="causal (the headline is non-causal)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--variant-calls", type=int, default=100)
+    ap.add_argument("--only-kernel", action="store_true", help="just the timed loop (for profilers)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the kernel runs on one GPU's share of heads and needs no "
+              "collective; multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    wl = qin.WORKLOADS[args.workload]
+    if args.dtype:
+        wl = wl.replace(dtype=args.dtype)
+    causal = bool(args.causal)
+    wl = wl.replace(causal=causal)
+    x = qin.make_inputs(wl)
+    dev_t = tuple(t.cuda() for t in (x.q, x.k, x.v))
+    B, H, N, d = x.q.shape
+    odt = torch.float32 if x.q.dtype == torch.float32 else torch.bfloat16
+    out = torch.empty((B, H, N, d), dtype=odt, device="cuda")
+    var = {"kind": args.kind}
+    if args.kind in ("pot", "kint"):
+        var["levels"] = args.levels
+    if args.window is not None:
+        var["window"] = args.window
+    if args.interp:
+        var["interp"] = True
+    dtn = DT_NAME[x.q.dtype]
+
+    fn = lambda: call(dev_t, x, var, causal, out)  # noqa: E731
+    if args.only_kernel:
+        ms, _ = time_loop(fn, args.steps, args.warmup)
+        print(json.dumps({"ms_per_launch": ms}))
+        return 0
+
+    torch.cuda.synchronize()
+    ms, wall = time_loop(fn, args.steps, args.warmup)
+    P = pairs(B, H, N, causal)
+    credited = 4 * d * P
+    tflops = credited / (ms * 1e-3) / 1e12
+    alg = mfma_flops_per_pair(args.kind, d) * P
+    achieved = alg / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtn]
+    rec = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtn, "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "Hkv": x.k.shape[1], "N": N, "d": d, "causal": causal,
+                   "variant": var, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2),
+        "pct_own_dtype_peak": round(100 * tflops / peak, 2),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(wl.name, dtn, var, causal, alg),
+                     "flops_per_launch": alg, "flops_per_pair": mfma_flops_per_pair(args.kind, d)},
+    }
+
+    if not args.no_variants:
+        table = {}
+        for vname, vv in [("exact_online", {"kind": "exact"}), ("exact_anchored", {"kind": "exact_anchored"}),
+                          ("pot16", {"kind": "pot", "levels": 16}), ("pot8", {"kind": "pot", "levels": 8}),
+                          ("kint16_window8_hard", {"kind": "kint", "levels": 16, "window": 8.0}),
+                          ("kint16_minmax_hard", {"kind": "kint", "levels": 16}),
+                          ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True})]:
+            for c in (False, True):
+                t, host = time_calls(lambda: call(dev_t, x, vv, c, out), args.variant_calls)
+                Pc = pairs(B, H, N, c)
+                med = float(np.median(t))
+                table[f"{vname}:{'causal' if c else 'noncausal'}"] = {
+                    "median_ms": round(med, 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+                    "p90_ms": round(float(np.percentile(t, 90)), 5), "host_call_ms": round(host, 5),
+                    "tflops": round(4 * d * Pc / (med * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100 * 4 * d * Pc / (med * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2)}
+        rec["variants"] = table
+        for c in ("noncausal", "causal"):
+            p, e = table[f"pot16:{c}"], table[f"exact_anchored:{c}"]
+            rec.setdefault("pot_vs_exact_anchored", {})[c] = {
+                "speedup": round(e["median_ms"] / p["median_ms"], 4),
+                "disjoint_p10_p90": p["p90_ms"] < e["p10_ms"]}
+            eo = table[f"exact_online:{c}"]
+            rec.setdefault("pot_vs_exact_online", {})[c] = {"speedup": round(eo["median_ms"] / p["median_ms"], 4)}
+        rec["b200_context"] = {"fp8_8k_causal_speedup_pct": 12.4, "fp8_8k_noncausal_speedup_pct": 25.8,
+                               "note": "the pages' B200 FlashAttention-4 figures; context, not a target"}
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, var, causal, args.cpu_seconds)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+/*
+ * qsa.h -- C ABI of libqsa, the quantized-softmax attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One operation: the fused attention forward
+ *
+ *     O = softmax~(scale * Q K^T) V
+ *
+ * in which the exponential inside softmax is either exact (the control) or
+ * replaced by a coarse grid anchored at each row's maximum:
+ *
+ *   - K-interval attention: the exponential is read off K+1 grid values
+ *     fitted to each row of scores, with per-row min-max or fixed-window
+ *     calibration and hard rounding or interpolation ("Pretraining
+ *     Transformers with Quantized Softmax in Attention", abstract; chapter 1
+ *     "The problem"; chapter 5 "Build the method").
+ *   - Rowmax-PoT: power-of-two weights 2^-e, e = rint((m - s) log2 e) clipped
+ *     to L levels, anchored at each row maximum ("Approximating Softmax in
+ *     Pretrained LLMs: Model Sensitivity and Kernel Acceleration", abstract;
+ *     the wiki summary's flowchart: QK tile -> row max -> power-of-two
+ *     weights -> PV matmul -> output).
+ *
+ * Notation: s_ij = scale * q_i . k_j; m_i and mn_i are the maximum and the
+ * minimum of s_ij over the keys visible to row i (causal: j <= i, top-left
+ * aligned; otherwise all j).  O_i = sum_j w_ij v_j / sum_j w_ij.
+ *
+ * Conventions shared by every entry point
+ *   Layout    Q and O are [B, H, N, d], K and V are [B, Hkv, N, d], all
+ *             contiguous with d innermost.  Query head h reads KV head
+ *             h / (H / Hkv) (grouped-query attention when Hkv < H).
+ *   Types     dtype QSA_DT_F32: Q, K, V and O are float32.
+ *             dtype QSA_DT_BF16: Q, K, V and O are bfloat16.
+ *             dtype QSA_DT_FP8_E4M3: Q, K, V are OCP FP8 E4M3 ("fn": no
+ *             infinities, max 448) with per-tensor descales (see
+ *             qsa_fwd_ex_opts); O is bfloat16.
+ *   Pointers  Q, K, V, O and every optional output are DEVICE pointers owned
+ *             by the caller.  The library allocates nothing, keeps no state
+ *             between calls and needs no workspace.
+ *   Streams   `stream` is a hipStream_t passed as void* (NULL: the null
+ *             stream).  A call only enqueues work and returns; the caller
+ *             synchronises.  Calls are reentrant and thread-safe.
+ *   Errors    The return value is a qsa_status.  Arguments are validated on
+ *             the host before any HIP call; nothing is launched when
+ *             validation fails.  Launch failures return QSA_ERR_HIP.  Faults
+ *             raised later by the asynchronous kernel surface at the caller's
+ *             next synchronisation.  qsa_last_error() gives a thread-local
+ *             text for the most recent failure on the calling thread.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_VERSION 1
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                        */
+  QSA_ERR_SHAPE = 2,       /* B, H, Hkv or N out of range, H % Hkv != 0, ...    */
+  QSA_ERR_PARAM = 3,       /* k_levels, window, scale or descale out of range   */
+  QSA_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement     */
+  QSA_ERR_HIP = 5          /* the HIP runtime reported an error at launch       */
+} qsa_status;
+
+typedef enum {
+  QSA_DT_F32 = 0,
+  QSA_DT_BF16 = 1,
+  QSA_DT_FP8_E4M3 = 2
+} qsa_dtype;
+
+/*
+ * variant = one base kind | any flags.
+ *
+ * QSA_EXACT           exact softmax with an online (running) maximum: the
+ *                     control, w = exp(s - m).  One pass over the keys.
+ * QSA_KINT            K-interval attention with K = k_levels intervals, i.e.
+ *                     K+1 grid values T_l = exp(-l*Delta), Delta = (m - lo)/K,
+ *                     l = 0..K.  Calibration lo = mn (min-max, default) or
+ *                     lo = m - window (QSA_F_WINDOW).  With y = (m - s)/Delta:
+ *                     hard rounding w = T_min(rint(y), K) (default) or linear
+ *                     interpolation between T_floor(y) and T_floor(y)+1
+ *                     (QSA_F_INTERP).  A min-max row whose visible scores are
+ *                     all equal (Delta = 0) gives every visible key weight 1.
+ * QSA_POT             Rowmax-PoT with L = k_levels levels: e = rint((m - s)
+ *                     log2 e), saturated at L-1, w = 2^-e.
+ * QSA_EXACT_ANCHORED  exact softmax anchored at the true row maximum found by
+ *                     the same pre-pass the grid variants use, w = exp(s - m)
+ *                     with no running rescale: the grid kernels with the
+ *                     exponential put back, for like-for-like timing.
+ *
+ * QSA_F_INTERP        K-interval only: linear interpolation.
+ * QSA_F_WINDOW        K-interval only: fixed-window calibration [m - window, m].
+ * QSA_F_FLUSH         K-interval (window) and PoT: scores outside the grid
+ *                     (K-interval: s < m - window; PoT: e >= L) get weight 0
+ *                     instead of the last grid value.
+ *
+ * rint is round-half-to-even.  The row maximum always gets weight exactly 1.
+ */
+enum {
+  QSA_EXACT = 0,
+  QSA_KINT = 1,
+  QSA_POT = 2,
+  QSA_EXACT_ANCHORED = 3,
+  QSA_BASE_MASK = 0x0F,
+  QSA_F_INTERP = 1 << 4,
+  QSA_F_WINDOW = 1 << 5,
+  QSA_F_FLUSH = 1 << 6
+};
+
+/* Index codes written to qsa_fwd_ex_opts.grid_idx for elements without a grid index. */
+#define QSA_IDX_FLUSHED 254u
+#define QSA_IDX_MASKED 255u
+
+/*
+ * Limits checked by validation:
+ *   1 <= B, H, Hkv;  H % Hkv == 0;  1 <= N <= 2^20;  d in {64, 128};
+ *   B*H*N*d < 2^31 and B*Hkv*N*d < 2^31 (element offsets are 32-bit);
+ *   QSA_KINT: 1 <= k_levels <= 64;  QSA_POT: 1 <= k_levels <= 64
+ *   (fp8: k_levels <= 16, so the power-of-two weights stay exact in the
+ *   8-bit operand of the PV product);
+ *   QSA_F_WINDOW: window finite and > 0;  flags only on the kinds above.
+ */
+
+/*
+ * qsa_attn_fwd -- the attention forward.
+ *
+ *   Q, K, V   device inputs in the layout and dtype above.
+ *   O         device output [B, H, N, d] (float32 for QSA_DT_F32, else bf16).
+ *   B, H, Hkv batch, query heads, key/value heads.
+ *   N         sequence length (queries and keys; causal is top-left aligned).
+ *   d         head dimension, 64 or 128.
+ *   causal    nonzero: key j is visible to query i only when j <= i.
+ *   variant   base kind | flags (above).
+ *   k_levels  K (K-interval intervals) or L (PoT levels); ignored by the
+ *             exact kinds.
+ *   window    W for QSA_F_WINDOW, in units of the scaled score; else ignored.
+ *   dtype     a qsa_dtype.
+ *   stream    hipStream_t or NULL.
+ * scale = 1/sqrt(d); fp8 descales 1.  Returns a qsa_status.
+ */
+int qsa_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                 int B, int H, int Hkv, int N, int d, int causal,
+                 int variant, int k_levels, float window, int dtype, void* stream);
+
+/* Optional arguments and diagnostic outputs of qsa_attn_fwd_ex.  Zero-initialise
+ * the struct and set what you need; every pointer is a device pointer or NULL. */
+typedef struct {
+  float scale;                 /* score scale; 0 -> 1/sqrt(d); must be finite and >= 0 */
+  float q_descale;             /* fp8 per-tensor descales: stored value * descale = real */
+  float k_descale;             /*   value; 0 -> 1.  Must be 1 or 0 for non-fp8 dtypes.   */
+  float v_descale;
+  float* row_max;              /* [B,H,N] float32: m_i (the anchor).                     */
+  float* row_lo;               /* [B,H,N] float32: K-interval: the calibrated lower end  */
+                               /*   lo_i; other anchored kinds: the visible row minimum. */
+                               /*   Not available for QSA_EXACT (must be NULL).          */
+  float* row_sum;              /* [B,H,N] float32: l_i = sum_j w_ij of the weights that  */
+                               /*   entered the PV product (QSA_EXACT: relative to the   */
+                               /*   final running maximum).                              */
+  unsigned char* grid_idx;     /* [B,H,idx_rows,N] u8: per element the grid index l (K-  */
+                               /*   interval; interpolation: floor(y) clipped to K) or   */
+                               /*   the exponent e (PoT); 0 for exact kinds;             */
+                               /*   QSA_IDX_FLUSHED / QSA_IDX_MASKED otherwise.          */
+  int idx_row0;                /* first query row dumped into grid_idx                   */
+  int idx_rows;                /* number of query rows dumped (0: none)                  */
+} qsa_fwd_ex_opts;
+
+/*
+ * qsa_attn_fwd_ex -- qsa_attn_fwd with the options above (opts may be NULL,
+ * which is qsa_attn_fwd).  The diagnostic outputs cost extra stores; the grid
+ * index dump is meant for parity checks.  grid_idx requires idx_row0 >= 0,
+ * idx_rows >= 1, idx_row0 + idx_rows <= N and B*H*idx_rows*N < 2^31.
+ */
+int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O,
+                    int B, int H, int Hkv, int N, int d, int causal,
+                    int variant, int k_levels, float window, int dtype,
+                    const qsa_fwd_ex_opts* opts, void* stream);
+
+/* Host-only validation of the scalar arguments of qsa_attn_fwd (no HIP call,
+ * no pointer check).  Returns the status qsa_attn_fwd would return. */
+int qsa_attn_validate(int B, int H, int Hkv, int N, int d, int causal,
+                      int variant, int k_levels, float window, int dtype);
+
+/* Static text for a status code ("QSA_OK", ...); never NULL. */
+const char* qsa_status_string(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none).  The
+ * pointer stays valid until the next qsa_* call on the same thread. */
+const char* qsa_last_error(void);
+
+/* QSA_VERSION of the library. */
+int qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,207 @@
+// Per-element weight functions of the quantized-softmax attention forward
+// (device code shared by every kernel of libqsa).
+//
+// Every function takes the raw score accumulator `acc` (the dot product of a
+// query and a key in the units the MMA produced) and per-row constants in the
+// same units, so the score scale is folded into the constants once per row:
+//
+//   y = (M - acc) * c     M = row maximum of acc over the visible keys
+//
+// exact / PoT: c = scale * log2(e), so y = (m - s) log2(e);
+// K-interval:  c = scale / Delta,   so y = (m - s) / Delta.
+//
+// Rowmax-PoT ("Approximating Softmax in Pretrained LLMs", abstract; the wiki
+// summary's flowchart "Row max -> Power-of-two weights"): w = 2^-e with
+// e = rint(y) clipped to L-1.  The weight is built in the float's exponent
+// field with integer operations; no exponential is evaluated.
+//
+// K-interval attention ("Pretraining Transformers with Quantized Softmax in
+// Attention", abstract and chapter 1): w is read off a table of K+1 grid
+// values T_l = exp(-l Delta) kept per row in LDS; hard rounding takes the
+// nearest grid point, interpolation the straight line between neighbours.
+#pragma once
+
+#include "qsa_common.h"
+
+namespace qsa {
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-row constants.
+struct RowC {
+  float c;      // multiplier on (M - acc)
+  float mc;     // M * c
+  uint32_t tab; // K-interval: byte offset of this row's column in the LDS table
+};
+
+// Table layout (K-interval): entry l of local row r sits at byte
+// (l * ROWS + r) * 4 (hard: T_l) or (l * ROWS + r) * 8 (interpolation:
+// T_l, T_{l+1} - T_l).  Consecutive rows fall in consecutive banks, so the
+// 32 rows of a half-wave look up their own tables without bank conflicts.
+// SH = log2(ROWS * 4).
+
+template <int WK> struct Weight;
+
+// Exact exponential (both the online control and the anchored variant).
+template <int WK> struct ExactW {
+  template <int SH>
+  static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char*, int) {
+    return __builtin_amdgcn_exp2f(fmaf(acc, r.c, -r.mc));
+  }
+  static __device__ __forceinline__ uint32_t idx(float, const RowC&, int) { return 0u; }
+};
+template <> struct Weight<WK_EXACT> : ExactW<WK_EXACT> {};
+template <> struct Weight<WK_EXACT_ANCH> : ExactW<WK_EXACT_ANCH> {};
+
+// Rowmax-PoT.  t = 2^24 - y is rounded by the subtraction itself to an
+// integer (the float spacing in [2^23, 2^24] is 1), ties to even; since 2^24
+// is even, t and e = 2^24 - t have the same parity, so e = rint(y) with ties
+// to even.  bits(t) = 0x4B800000 - e, and shifting it left by 23 leaves
+// -e << 23 (the exponent bits of 2^24 shift out), so adding 127 << 23 gives the
+// binary32 pattern of 2^-e.  The clip e <= L-1 is an integer max on bits(t).
+template <bool FLUSH> struct PotW {
+  template <int SH>
+  static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char*, int L) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    int32_t tb = (int32_t)fbits(16777216.0f - y);
+    const int32_t lo = 0x4B800000 - (L - 1);
+    if (FLUSH) {
+      if (tb < lo) return 0.0f;
+    } else {
+      tb = tb > lo ? tb : lo;
+    }
+    return bitsf(((uint32_t)tb << 23) + (127u << 23));
+  }
+  static __device__ __forceinline__ uint32_t idx(float acc, const RowC& r, int L) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    int32_t tb = (int32_t)fbits(16777216.0f - y);
+    const int32_t lo = 0x4B800000 - (L - 1);
+    if (tb < lo) return FLUSH ? 254u : (uint32_t)(L - 1);
+    return (uint32_t)(0x4B800000 - tb);
+  }
+};
+template <> struct Weight<WK_POT> : PotW<false> {};
+template <> struct Weight<WK_POT_FLUSH> : PotW<true> {};
+
+// K-interval, hard rounding.  t = y + 2^23 rounds y to the nearest integer
+// (ties to even) inside the float: bits(t) = 0x4B000000 + l.  The clip l <= K
+// is an integer min; (bits(t) << SH) drops the 0x4B000000 part (SH >= 8) and
+// leaves l * ROWS * 4, the table offset of entry l.
+template <bool FLUSH> struct KHardW {
+  template <int SH>
+  static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char* tab, int K) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    int32_t tb = (int32_t)fbits(y + 8388608.0f);
+    const int32_t hi = 0x4B000000 + K;
+    tb = tb < hi ? tb : hi;
+    tb = tb > 0x4B000000 ? tb : 0x4B000000;   // y >= 0 up to rounding; keeps the lookup in the table
+    const float wv = *(const float*)(tab + (((uint32_t)tb << SH) + r.tab));
+    if (FLUSH && y > (float)K) return 0.0f;
+    return wv;
+  }
+  static __device__ __forceinline__ uint32_t idx(float acc, const RowC& r, int K) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    if (FLUSH && y > (float)K) return 254u;
+    int32_t tb = (int32_t)fbits(y + 8388608.0f);
+    const int32_t hi = 0x4B000000 + K;
+    tb = tb < hi ? tb : hi;
+    tb = tb > 0x4B000000 ? tb : 0x4B000000;
+    return (uint32_t)(tb - 0x4B000000);
+  }
+};
+template <> struct Weight<WK_KH> : KHardW<false> {};
+template <> struct Weight<WK_KH_FLUSH> : KHardW<true> {};
+
+// K-interval, linear interpolation between T_l and T_{l+1}, l = floor(y)
+// (y clipped to [0, K]; at y = K the slope entry is 0, giving T_K).
+template <bool FLUSH> struct KInterpW {
+  template <int SH>
+  static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char* tab, int K) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, (float)K);
+    const float fl = __builtin_floorf(yc);
+    const float t = yc - fl;
+    const uint32_t l = (uint32_t)(int32_t)fl;
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 e = *(const f2*)(tab + ((l << (SH + 1)) + r.tab));
+    if (FLUSH && y > (float)K) return 0.0f;
+    return fmaf(t, e.y, e.x);
+  }
+  static __device__ __forceinline__ uint32_t idx(float acc, const RowC& r, int K) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    if (FLUSH && y > (float)K) return 254u;
+    const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, (float)K);
+    return (uint32_t)(int32_t)__builtin_floorf(yc);
+  }
+};
+template <> struct Weight<WK_KI> : KInterpW<false> {};
+template <> struct Weight<WK_KI_FLUSH> : KInterpW<true> {};
+
+// Per-row constants from the pre-pass extrema (raw units) and, for
+// K-interval, the row's grid table written into LDS.  The K+1 table entries
+// are split between the `nsplit` lanes that share a row (this lane writes
+// entries part, part + nsplit, ...).
+template <int WK, int SH>
+__device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, int row_local,
+                                         unsigned char* tab, int part, int nsplit) {
+  RowC rc;
+  rc.tab = 0;
+  if (WK < WK_KH) {
+    rc.c = a.sc * kLog2e;
+    rc.mc = M * rc.c;
+    return rc;
+  }
+  const int K = a.levels;
+  float delta_s;  // grid step in score units
+  if (a.window_calib) {
+    delta_s = a.window / (float)K;
+    rc.c = a.sc * (float)K / a.window;
+  } else {
+    const float range = M - MN;
+    rc.c = range > 0.0f ? (float)K / range : 0.0f;  // zero-width grid: every weight T_0 = 1
+    delta_s = range * a.sc / (float)K;
+  }
+  rc.mc = M * rc.c;
+  const float step = -delta_s * kLog2e;
+  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH);
+  constexpr int ROWS = (1 << SH) / 4;
+  rc.tab = (uint32_t)row_local * (INTERP ? 8u : 4u);
+  for (int l = part; l <= K; l += nsplit) {
+    const float t0 = __builtin_amdgcn_exp2f(step * (float)l);
+    if (INTERP) {
+      const float t1 = (l < K) ? __builtin_amdgcn_exp2f(step * (float)(l + 1)) : t0;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      *(f2*)(tab + ((size_t)l * ROWS + row_local) * 8) = f2{t0, t1 - t0};
+    } else {
+      *(float*)(tab + ((size_t)l * ROWS + row_local) * 4) = t0;
+    }
+  }
+  return rc;
+}
+
+// Table bytes a workgroup of ROWS rows needs for weight kind WK.
+__host__ __device__ inline size_t table_bytes(int wk, int rows, int K) {
+  if (wk == WK_KH || wk == WK_KH_FLUSH) return (size_t)rows * (K + 1) * 4;
+  if (wk == WK_KI || wk == WK_KI_FLUSH) return (size_t)rows * (K + 1) * 8;
+  return 0;
+}
+
+// Block index -> (batch*head, query tile).  Workgroups are dispatched round-
+// robin over the 8 XCDs (workgroup w runs on XCD w % 8); the remap gives each
+// XCD a contiguous range of logical tiles, so the query tiles of one head
+// share an XCD and its L2 while they sweep the same K/V.  Causal launches
+// take the longest (last) query tiles of each head first.
+__device__ __forceinline__ void map_block(const FwdArgs& a, int& bh, int& qt) {
+  const int L = blockIdx.x, T = a.total_blocks;
+  const int x = L & 7, slot = L >> 3;
+  const int per = T >> 3, rem = T & 7;
+  const int logical = x * per + (x < rem ? x : rem) + slot;
+  bh = logical / a.n_qtiles;
+  const int t = logical - bh * a.n_qtiles;
+  qt = a.causal ? (a.n_qtiles - 1 - t) : t;
+}
+
+}  // namespace qsa

@@ -1,0 +1,168 @@
+"""GPU-vs-oracle comparison protocol (test helper).
+
+The GPU forms scores in fp32 (MFMA accumulation of exact bf16/fp8 products,
+or fp32 FMAs); the oracle in float64.  For a row i the fp32 score error is
+bounded by delta*_i = gamma * scale * max_j sum_c |q_ic k_jc| with
+gamma = 2 d u, u = 2^-24 (twice the textbook bound for any summation order).
+That error moves the grid coordinate y_ij by at most eps_ij (below), so an
+element whose y lies within eps of a discontinuity of its weight function is
+edge-ambiguous: either neighbouring grid index is a correct result.
+
+Checks:
+  * index agreement >= 99.9 % over visible elements, and every disagreement
+    edge-ambiguous; masked codes identical;
+  * per row ||O_gpu - O_ref|| <= tol ||O_ref|| + sigma_i, where sigma_i is the
+    exact worst-case move of O_i if every ambiguous element took its other
+    index.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+
+U = 2.0 ** -24
+LOG2E = 1.0 / math.log(2.0)
+
+
+@dataclass
+class Report:
+    rows: int = 0
+    elems: int = 0
+    idx_agree: float = 1.0
+    idx_disagree: int = 0
+    idx_bad: int = 0              # disagreements outside the ambiguity band
+    amb_rows: int = 0
+    max_rel_err: float = 0.0      # max over rows of ||dO|| / ||O_ref||
+    max_excess: float = 0.0       # max over rows of ||dO|| - tol ||O_ref|| - sigma (<= 0 passes)
+    notes: list = field(default_factory=list)
+
+    def merge(self, o: "Report"):
+        tot = self.elems + o.elems
+        if tot:
+            self.idx_agree = (self.idx_agree * self.elems + o.idx_agree * o.elems) / tot
+        self.elems = tot
+        self.rows += o.rows
+        self.idx_disagree += o.idx_disagree
+        self.idx_bad += o.idx_bad
+        self.amb_rows += o.amb_rows
+        self.max_rel_err = max(self.max_rel_err, o.max_rel_err)
+        self.max_excess = max(self.max_excess, o.max_excess)
+
+
+def _edges(var, y, K):
+    """Distance of y to the nearest discontinuity of the weight (and the index)."""
+    kind = var["kind"]
+    if kind == "exact":
+        return np.full_like(y, np.inf), np.full_like(y, np.inf)
+    frac_half = np.abs(y - np.floor(y) - 0.5)                   # distance to a half-integer
+    if kind == "pot" or not var.get("interp", False):
+        d_w = frac_half
+        if var.get("flush") and kind == "kint":
+            d_w = np.minimum(d_w, np.abs(y - K))
+        return d_w, d_w
+    # interpolation: weight continuous inside the grid; index = floor(y) jumps at integers
+    d_w = np.abs(y - K) if var.get("flush") else np.full_like(y, np.inf)
+    d_i = np.minimum(np.abs(y - np.rint(y)), d_w)
+    return d_w, d_i
+
+
+def _eps(var, y, m, S, dstar, delta):
+    kind = var["kind"]
+    if kind == "exact":
+        return np.zeros_like(y)
+    base = 4 * U * (np.abs(m)[:, None] + np.abs(S))
+    if kind == "pot":
+        return (2 * dstar[:, None] + base) * LOG2E + 4 * U * np.abs(y)
+    K = var["levels"]
+    grow = 0.0 if var.get("window") is not None else (np.abs(y) / K)
+    dd = np.where(delta > 0, delta, np.inf)[:, None]
+    return (2 * dstar[:, None] * (1 + grow) + base) / dd + 4 * U * np.abs(y)
+
+
+def _other_weight(var, idx, y, T):
+    """Weight an ambiguous element gets if it lands across its nearest edge."""
+    kind = var["kind"]
+    fl = np.floor(y)
+    other = np.where(y - fl < 0.5, fl + 1, fl)          # index across the nearest half-integer
+    if kind == "pot":
+        L = var["levels"]
+        other = np.maximum(other, 0)
+        if var.get("flush"):
+            return np.where(other >= L, 0.0, np.exp2(-np.minimum(other, L - 1)))
+        return np.exp2(-np.minimum(other, L - 1))
+    K = var["levels"]
+    flush = var.get("flush", False)
+    if var.get("interp"):
+        # inside the grid the weight is continuous; only the flush edge y = K jumps
+        return np.where(y <= K, 0.0, T[:, K:K + 1]) if flush else np.zeros_like(y)
+    oi = np.clip(other, 0, K).astype(np.int64)
+    w_other = np.take_along_axis(T, oi, axis=1)
+    if flush:
+        near_flush = np.abs(y - K) < np.abs(y - (fl + 0.5))
+        w_other = np.where(near_flush, np.where(y <= K, 0.0, T[:, K:K + 1]), w_other)
+        w_other = np.where((y > K) & ~near_flush, 0.0, w_other)
+    return w_other
+
+
+def compare_head(var, q, k, v, rows, O_gpu, idx_gpu=None, *, causal, scale=None, tol=1e-2, min_agree=0.999,
+                 l_gpu=None):
+    """Compare one (batch, head): q (Nq,d), k/v (N,d) float64 as stored (decoded,
+    descaled); rows: query rows; O_gpu (R,d) float; idx_gpu (R,N) uint8 or None."""
+    d = q.shape[1]
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    ref = oracle.head_rows(q, k, v, rows, causal=causal, detail=True, scale=scale,
+                           **{kk: var[kk] for kk in var if kk != "kind"}, kind=var["kind"])
+    R, N = ref["w"].shape
+    rep = Report(rows=R)
+    S = sc * (q[rows] @ k.T)
+    vis = ref["idx"] != oracle.IDX_MASKED
+    dstar = 2 * d * U * sc * np.max(np.abs(q[rows]) @ np.abs(k).T, axis=1)
+    K = var.get("levels") or 0
+    y = np.where(vis, ref["y"], 0.0)
+    d_w, d_i = _edges(var, y, K)
+    eps = _eps(var, y, ref["m"], S, dstar, ref["delta"])
+    amb_w = vis & (d_w <= eps)
+    amb_i = vis & (d_i <= eps)
+    if idx_gpu is not None and var["kind"] != "exact":
+        assert np.array_equal(idx_gpu == oracle.IDX_MASKED, ~vis), "masked positions differ"
+        dis = vis & (idx_gpu != ref["idx"])
+        rep.elems = int(vis.sum())
+        rep.idx_disagree = int(dis.sum())
+        rep.idx_agree = 1.0 - rep.idx_disagree / max(rep.elems, 1)
+        rep.idx_bad = int((dis & ~amb_i).sum())
+    # O: per-row relative error with the ambiguity slack
+    T = None
+    if var["kind"] == "kint":
+        T = np.exp(-np.arange(K + 1)[None, :] * ref["delta"][:, None])
+    sigma = np.zeros(R)
+    dw_sum = np.zeros(R)
+    if amb_w.any():
+        wo = _other_weight(var, ref["idx"], y, T)
+        dw = np.where(amb_w, np.abs(wo - ref["w"]), 0.0)
+        spread = np.linalg.norm(v[None, :, :] - ref["O"][:, None, :], axis=2) if R * N * d < 5e7 else None
+        if spread is None:
+            spread = np.stack([np.linalg.norm(v - ref["O"][i], axis=1) for i in range(R)])
+        num = (dw * spread).sum(1)
+        den = ref["l"] - dw.sum(1)
+        sigma = np.where(den > 0, num / np.maximum(den, 1e-300), np.inf)
+        rep.amb_rows = int((dw.sum(1) > 0).sum())
+        dw_sum = dw.sum(1)
+    err = np.linalg.norm(O_gpu.astype(np.float64) - ref["O"], axis=1)
+    nrm = np.linalg.norm(ref["O"], axis=1)
+    rep.max_rel_err = float(np.max(err / np.maximum(nrm, 1e-30)))
+    rep.max_excess = float(np.max(err - tol * nrm - sigma))
+    if idx_gpu is not None and var["kind"] != "exact":
+        assert rep.idx_bad == 0, f"{rep.idx_bad} index disagreements outside the fp32 edge band"
+        # interpolation's index floor(y) is informative only: its weight is continuous there,
+        # and min-max rows put their minimum exactly on the integer y = K
+        if not var.get("interp"):
+            assert rep.idx_agree >= min_agree, f"index agreement {rep.idx_agree:.5f} < {min_agree}"
+    assert rep.max_excess <= 0, f"O error exceeds tol: max rel err {rep.max_rel_err:.3e}"
+    if l_gpu is not None:   # row sums: same tolerance plus the weight change of ambiguous elements
+        excess = np.abs(np.asarray(l_gpu, np.float64) - ref["l"]) - tol * ref["l"] - dw_sum
+        assert np.all(excess <= 0), f"row sum off by {np.max(excess):.3e} beyond tolerance"
+    return rep, ref

@@ -1,0 +1,146 @@
+"""The C ABI loads and validates on the host (no GPU, no compute calls).
+
+Every function declared in include/qsa.h must be exported by libqsa.so, and
+every validation rule must return its documented status before any HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import quantized_softmax_approximation_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qsa.lib_path()), reason="libqsa.so not built")
+
+GOOD = dict(B=1, H=4, Hkv=2, N=100, d=64, causal=1, variant=qsa.POT, k_levels=8, window=0.0, dtype=qsa.DT_BF16)
+
+
+def v(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return qsa.attn_validate(a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"], a["variant"], a["k_levels"],
+                             a["window"], a["dtype"])
+
+
+def test_every_declared_symbol_is_exported():
+    src = open(HEADER).read()
+    names = re.findall(r"^\s*(?:int|const char\*)\s+(qsa_\w+)\s*\(", src, flags=re.M)
+    assert set(names) == {"qsa_attn_fwd", "qsa_attn_fwd_ex", "qsa_attn_validate", "qsa_status_string",
+                          "qsa_last_error", "qsa_version"}
+    L = ctypes.CDLL(qsa.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert qsa.version() == 1
+    assert qsa.status_string(0) == "QSA_OK"
+    assert [qsa.status_string(i) for i in range(1, 6)] == [
+        "QSA_ERR_NULL_PTR", "QSA_ERR_SHAPE", "QSA_ERR_PARAM", "QSA_ERR_UNSUPPORTED", "QSA_ERR_HIP"]
+    assert qsa.status_string(99) == "QSA_ERR_UNKNOWN"
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    for name, val in [("QSA_EXACT", qsa.EXACT), ("QSA_KINT", qsa.KINT), ("QSA_POT", qsa.POT),
+                      ("QSA_EXACT_ANCHORED", qsa.EXACT_ANCHORED), ("QSA_DT_F32", qsa.DT_F32),
+                      ("QSA_DT_BF16", qsa.DT_BF16), ("QSA_DT_FP8_E4M3", qsa.DT_FP8_E4M3)]:
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == val, name
+    for name, val in [("QSA_F_INTERP", qsa.F_INTERP), ("QSA_F_WINDOW", qsa.F_WINDOW), ("QSA_F_FLUSH", qsa.F_FLUSH)]:
+        m = re.search(rf"\b{name}\s*=\s*1\s*<<\s*(\d+)", src)
+        assert m and (1 << int(m.group(1))) == val, name
+
+
+def test_valid_arguments():
+    assert v() == qsa.OK
+    assert qsa.last_error() == ""
+    for var, kl, w in [(qsa.EXACT, 0, 0.0), (qsa.EXACT_ANCHORED, 0, 0.0), (qsa.KINT, 4, 0.0),
+                       (qsa.KINT | qsa.F_INTERP, 16, 0.0), (qsa.KINT | qsa.F_WINDOW, 16, 8.0),
+                       (qsa.KINT | qsa.F_WINDOW | qsa.F_FLUSH | qsa.F_INTERP, 64, 8.0),
+                       (qsa.POT | qsa.F_FLUSH, 64, 0.0), (qsa.POT, 1, 0.0)]:
+        assert v(variant=var, k_levels=kl, window=w) == qsa.OK, (var, kl, w)
+    assert v(d=128, N=1, H=64, Hkv=8) == qsa.OK
+    assert v(dtype=qsa.DT_F32) == qsa.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), qsa.ERR_SHAPE), (dict(H=0), qsa.ERR_SHAPE), (dict(Hkv=0), qsa.ERR_SHAPE), (dict(N=0), qsa.ERR_SHAPE),
+    (dict(H=6, Hkv=4), qsa.ERR_SHAPE), (dict(N=(1 << 20) + 1), qsa.ERR_SHAPE), (dict(d=0), qsa.ERR_SHAPE),
+    (dict(d=96), qsa.ERR_UNSUPPORTED), (dict(d=256), qsa.ERR_UNSUPPORTED),
+    (dict(B=1024, H=64, N=65536, d=128), qsa.ERR_SHAPE),
+    (dict(dtype=3), qsa.ERR_PARAM), (dict(dtype=-1), qsa.ERR_PARAM),
+    (dict(variant=4), qsa.ERR_PARAM), (dict(variant=qsa.POT | (1 << 8)), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT | qsa.F_INTERP), qsa.ERR_PARAM), (dict(variant=qsa.POT | qsa.F_WINDOW, window=8.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.EXACT | qsa.F_FLUSH), qsa.ERR_PARAM),
+    (dict(variant=qsa.EXACT_ANCHORED | qsa.F_FLUSH), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT, k_levels=0), qsa.ERR_PARAM), (dict(variant=qsa.KINT, k_levels=65), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT, k_levels=0), qsa.ERR_PARAM), (dict(variant=qsa.POT, k_levels=65), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT, k_levels=17, dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT | qsa.F_WINDOW, k_levels=4, window=0.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT | qsa.F_WINDOW, k_levels=4, window=-1.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT | qsa.F_WINDOW, k_levels=4, window=math.inf), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT | qsa.F_WINDOW, k_levels=4, window=math.nan), qsa.ERR_PARAM),
+])
+def test_invalid_arguments(kw, status):
+    assert v(**kw) == status
+    assert qsa.last_error() != ""
+
+
+def _fwd(Q=1, K=1, V=1, O=1, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    L = qsa.lib()
+    return L.qsa_attn_fwd(Q, K, V, O, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"], a["variant"],
+                          a["k_levels"], a["window"], a["dtype"], None)
+
+
+def test_null_pointers_rejected_before_any_hip_call():
+    for args in [dict(Q=None), dict(K=None), dict(V=None), dict(O=None)]:
+        assert _fwd(**args) == qsa.ERR_NULL_PTR
+    # validation runs first: a bad shape wins over a NULL pointer
+    assert _fwd(Q=None, B=0) == qsa.ERR_SHAPE
+
+
+def _fwd_ex(opts, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    L = qsa.lib()
+    return L.qsa_attn_fwd_ex(1, 1, 1, 1, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"], a["variant"],
+                             a["k_levels"], a["window"], a["dtype"], ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("fields,kw,status", [
+    (dict(scale=-1.0), {}, qsa.ERR_PARAM), (dict(scale=math.inf), {}, qsa.ERR_PARAM),
+    (dict(scale=math.nan), {}, qsa.ERR_PARAM),
+    (dict(q_descale=2.0), {}, qsa.ERR_PARAM),                         # descale on bf16
+    (dict(v_descale=-1.0), dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
+    (dict(k_descale=math.inf), dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
+    (dict(row_lo=8), dict(variant=qsa.EXACT), qsa.ERR_PARAM),
+    (dict(grid_idx=8, idx_row0=0, idx_rows=0), {}, qsa.ERR_SHAPE),
+    (dict(grid_idx=8, idx_row0=-1, idx_rows=4), {}, qsa.ERR_SHAPE),
+    (dict(grid_idx=8, idx_row0=98, idx_rows=4), {}, qsa.ERR_SHAPE),
+    (dict(grid_idx=8, idx_row0=0, idx_rows=65536), dict(N=65536, H=64, Hkv=8, B=1), qsa.ERR_SHAPE),
+])
+def test_invalid_options(fields, kw, status):
+    o = qsa._Opts()
+    for k_, val in fields.items():
+        setattr(o, k_, val)
+    assert _fwd_ex(o, **kw) == status
+    assert qsa.last_error() != ""
+
+
+def test_binding_rejects_bad_tensors_on_host():
+    import torch
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        qsa.attn_fwd_ex(q, q, q)                      # CPU tensors
+    with pytest.raises(ValueError):
+        qsa.attn_fwd_ex(q, q[:, :, :4], q)            # shape mismatch
+    with pytest.raises(ValueError):
+        qsa.attn_fwd_ex(q, q.double(), q)             # dtype mismatch

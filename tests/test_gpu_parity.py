@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Inputs are the seeded synthetic workloads (quantized_softmax_approximation_amd
+.inputs); sizes run from the tiny fp32 case to the full long-context GQA
+workload (sampled row windows there), plus ragged tails, degenerate rows and
+the maximum sequence length.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_softmax_approximation_amd as qsa
+from quantized_softmax_approximation_amd import inputs as qin
+from tests import gpu_cases as gc
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qsa.lib()
+    yield
+
+
+# ---------------------------------------------------------------- tiny (fp32)
+
+TINY_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.KH4, gc.POT8, gc.POT4F, gc.KI4, gc.KH4W, gc.KI4W, gc.KH4WF, gc.KI4WF]
+
+
+@pytest.mark.parametrize("var", TINY_VARS, ids=gc.name)
+def test_tiny_fp32(var):
+    gc.run_parity(qin.WORKLOADS["tiny"], var)
+
+
+# ---------------------------------------------------------------- GPT-2 shaped (bf16, causal)
+
+GPT2_VARS = [gc.EXACT, gc.POT8, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KH16W, gc.KI4W, gc.KI16W]
+
+
+@pytest.fixture(scope="module")
+def gpt2():
+    wl = qin.WORKLOADS["gpt2"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("var", GPT2_VARS, ids=gc.name)
+def test_gpt2(gpt2, var):
+    wl, x, dev_t, f64 = gpt2
+    heads = [(0, 0), (3, 5), (7, 11)]
+    gc.run_parity(wl, var, heads=heads, x=x, dev_t=dev_t, f64=f64)
+
+
+# ---------------------------------------------------------------- 2K with attention sink (bf16, d=128)
+
+@pytest.fixture(scope="module")
+def pot2k():
+    wl = qin.WORKLOADS["pot2k"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT16, gc.KH16W], ids=gc.name)
+def test_pot2k(pot2k, var):
+    wl, x, dev_t, f64 = pot2k
+    gc.run_parity(wl, var, heads=[(0, 0), (2, 17), (3, 31)], x=x, dev_t=dev_t, f64=f64)
+
+
+# ---------------------------------------------------------------- long-context GQA (bf16, 16K, sampled rows)
+
+@pytest.fixture(scope="module")
+def gqa16k():
+    wl = qin.WORKLOADS["gqa16k"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT16, gc.KH4, gc.KH16, gc.KI16, gc.KH4W,
+                                 gc.KH16W, gc.KI4W], ids=gc.name)
+def test_gqa16k_sampled(gqa16k, var):
+    wl, x, dev_t, f64 = gqa16k
+    heads = [(0, 0), (0, 9), (0, 63)]
+    gc.run_parity(wl, var, heads=heads, windows=gc.sample_windows(wl.N, n=4, seed=5), x=x, dev_t=dev_t, f64=f64)
+
+
+# ---------------------------------------------------------------- ragged tails, tiny N, GQA, d
+
+EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 200, 333]
+
+
+@pytest.mark.parametrize("N", EDGE_N)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged(N, d, causal):
+    wl = qin.custom(f"ragged{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype="bf16", causal=causal, sigma_qk=1.5, seed=N + d)
+    x = qin.make_inputs(wl)
+    dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF):
+        gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 100])
+def test_ragged_fp32(N):
+    wl = qin.custom(f"f32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
+    x = qin.make_inputs(wl)
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W):
+        gc.run_parity(wl, var, x=x, verbose=False)
+
+
+def test_large_levels_and_windows():
+    wl = qin.custom("levels", B=1, H=2, N=300, d=64, dtype="bf16", causal=False, sigma_qk=2.0, seed=3)
+    x = qin.make_inputs(wl)
+    dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+    for var in (dict(kind="pot", levels=64), dict(kind="pot", levels=1), dict(kind="pot", levels=2, flush=True),
+                dict(kind="kint", levels=64), dict(kind="kint", levels=64, interp=True),
+                dict(kind="kint", levels=1), dict(kind="kint", levels=64, window=0.5, flush=True),
+                dict(kind="kint", levels=2, window=40.0, interp=True)):
+        gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64)
+
+
+def test_degenerate_rows_all_scores_equal():
+    # q = 0: every score is 0; min-max grids have zero width, all weights 1
+    wl = qin.custom("flat", B=1, H=2, N=130, d=64, dtype="bf16", causal=True, seed=4)
+    x = qin.make_inputs(wl)
+    x.q.zero_()
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4, gc.KH4W):
+        rep = gc.run_parity(wl, var, x=x, verbose=False)
+        assert rep.max_rel_err < 1e-2
+
+
+# ---------------------------------------------------------------- maximum sequence length
+
+@pytest.mark.parametrize("var", [gc.POT8, gc.EXACT], ids=gc.name)
+def test_max_sequence_length(var):
+    N = 1 << 20
+    wl = qin.custom("maxN", B=1, H=1, N=N, d=64, dtype="bf16", causal=True, sigma_qk=1.5, seed=11)
+    x = qin.make_inputs(wl)
+    gc.run_parity(wl, var, x=x, windows=[(0, 16), (N // 2 - 7, 16), (N - 16, 16)])
+
+
+# ---------------------------------------------------------------- properties
+
+def test_row_stats_match_oracle():
+    import oracle
+    wl = qin.custom("stats", B=1, H=2, N=257, d=128, dtype="bf16", causal=True, sigma_qk=1.5, seed=8)
+    x = qin.make_inputs(wl)
+    dev_t = gc.to_gpu(x)
+    qf, kf, vf = gc.decoded(x)
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KH4W, gc.EXACT_ANCH):
+        o, _, st = gc.gpu_call(x, dev_t, var, causal=True, stats=True)
+        for h in range(2):
+            ref = oracle.head_rows(qf[0, h], kf[0, h], vf[0, h], causal=True, **gc.oracle_var(var))
+            m = st["row_max"][0, h].cpu().numpy()
+            dstar = 2 * 128 * 2.0 ** -24 / np.sqrt(128) * np.max(np.abs(qf[0, h]) @ np.abs(kf[0, h]).T, axis=1)
+            assert np.all(np.abs(m - ref["m"]) <= dstar + 1e-6 * np.abs(ref["m"]))
+            l = st["row_sum"][0, h].cpu().numpy()    # online exact: relative to the final running max = m
+            parity.compare_head(gc.oracle_var(var), qf[0, h], kf[0, h], vf[0, h], np.arange(257),
+                                o[0, h].float().cpu().numpy(), causal=True, l_gpu=l)
+            if var["kind"] != "exact":
+                lo = st["row_lo"][0, h].cpu().numpy()
+                assert np.all(np.abs(lo - ref["lo"]) <= dstar + 1e-5 * (1 + np.abs(ref["lo"])))
+
+
+def test_deterministic_and_gqa_equals_repeated_kv():
+    wl = qin.custom("det", B=2, H=8, Hkv=2, N=300, d=128, dtype="bf16", causal=True, sigma_qk=1.5, seed=9)
+    x = qin.make_inputs(wl)
+    q, k, v = gc.to_gpu(x)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    for var in (gc.EXACT, gc.POT8, gc.KH16W, gc.KI4):
+        a = qsa.attn_fwd(q, k, v, causal=True, **var)
+        b = qsa.attn_fwd(q, k, v, causal=True, **var)
+        c = qsa.attn_fwd(q, kr, vr, causal=True, **var)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        assert torch.equal(a, c)
+
+
+def test_side_stream_and_out_argument():
+    wl = qin.custom("stream", B=1, H=2, N=200, d=64, dtype="bf16", causal=False, seed=10)
+    x = qin.make_inputs(wl)
+    q, k, v = gc.to_gpu(x)
+    ref = qsa.attn_fwd(q, k, v, kind="pot", levels=8)
+    s = torch.cuda.Stream()
+    out = torch.empty_like(ref)
+    with torch.cuda.stream(s):
+        qsa.attn_fwd(q, k, v, kind="pot", levels=8, out=out, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(ref, out)
+
+
+def test_errors_raise_without_launch():
+    q = torch.zeros(1, 3, 64, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(qsa.QSAError) as e:
+        qsa.attn_fwd(q, k, k, kind="pot", levels=8)
+    assert e.value.status == qsa.ERR_SHAPE
+    q96 = torch.zeros(1, 2, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(qsa.QSAError) as e:
+        qsa.attn_fwd(q96, q96, q96)
+    assert e.value.status == qsa.ERR_UNSUPPORTED
+    with pytest.raises(qsa.QSAError) as e:
+        qsa.attn_fwd(k, k, k, kind="kint", levels=0)
+    assert e.value.status == qsa.ERR_PARAM

@@ -1,0 +1,117 @@
+"""The GPU comparison protocol accepts a correct fp32 computation and rejects a wrong one.
+
+A float32 emulation of the kernels' arithmetic (fp32 scores accumulated in a
+different order, fp32 row constants, the same rounding steps) stands in for
+the GPU here.  It must pass `parity.compare_head` with every index
+disagreement inside the fp32 edge band, while a result with one wrong grid
+index outside the band, or a perturbed O, must fail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from tests import parity
+
+F = np.float32
+
+
+def emulate(var, q, k, v, causal):
+    """fp32 emulation of one head: scores in float32 (BLAS order), weights via fp32 ops."""
+    q32, k32, v32 = q.astype(F), k.astype(F), v.astype(F)
+    N, d = q.shape
+    sc = F(1.0 / math.sqrt(d))
+    acc = (q32 @ k32.T).astype(F)                               # raw dot products
+    vis = np.tril(np.ones((N, N), bool)) if causal else np.ones((N, N), bool)
+    M = np.where(vis, acc, -np.inf).max(1).astype(F)
+    MN = np.where(vis, acc, np.inf).min(1).astype(F)
+    kind = var["kind"]
+    idx = np.full((N, N), 255, np.uint8)
+    if kind == "exact":
+        c = F(sc * F(1.4426950408889634))
+        w = np.exp2((acc * c - M[:, None] * c).astype(F))
+        idx[vis] = 0
+    elif kind == "pot":
+        L = var["levels"]
+        c = F(sc * F(1.4426950408889634))
+        y = (M[:, None] * c - acc * c).astype(F)
+        e = np.rint(y)
+        if var.get("flush"):
+            kept = e <= L - 1
+            w = np.where(kept, np.exp2(-np.minimum(e, 126)), 0).astype(F)
+            idx = np.where(kept, e, 254).astype(np.uint8)
+        else:
+            e = np.clip(e, 0, L - 1)
+            w = np.exp2(-e).astype(F)
+            idx = e.astype(np.uint8)
+    else:
+        K = var["levels"]
+        if var.get("window") is not None:
+            W = F(var["window"])
+            c = np.full(N, F(sc * F(K) / W), F)
+            delta = np.full(N, F(W / F(K)), F)
+        else:
+            rng = (M - MN).astype(F)
+            c = np.where(rng > 0, F(K) / np.where(rng > 0, rng, 1), 0).astype(F)
+            delta = (rng * sc / F(K)).astype(F)
+        T = np.exp2(-np.arange(K + 1)[None, :] * (delta[:, None] * F(1.4426950408889634))).astype(F)
+        y = (M[:, None] * c[:, None] - acc * c[:, None]).astype(F)
+        rows = np.arange(N)[:, None]
+        if not var.get("interp"):
+            l = np.clip(np.rint(y), 0, K).astype(np.int64)
+            w = T[rows, l]
+            idx = l.astype(np.uint8)
+        else:
+            yc = np.clip(y, 0, K)
+            l = np.floor(yc).astype(np.int64)
+            t = (yc - l).astype(F)
+            Tn = np.concatenate([T, T[:, -1:]], axis=1)
+            w = (T[rows, l] + t * (Tn[rows, l + 1] - T[rows, l])).astype(F)
+            idx = l.astype(np.uint8)
+        if var.get("flush"):
+            w = np.where(y > K, 0, w).astype(F)
+            idx = np.where(y > K, 254, idx).astype(np.uint8)
+    w = np.where(vis, w, 0).astype(F)
+    idx = np.where(vis, idx, 255).astype(np.uint8)
+    O = (w @ v32) / w.sum(1, keepdims=True)
+    return O.astype(F), idx
+
+
+VARS = [dict(kind="exact"), dict(kind="pot", levels=8), dict(kind="pot", levels=4, flush=True),
+        dict(kind="kint", levels=4), dict(kind="kint", levels=16, interp=True),
+        dict(kind="kint", levels=4, window=8.0), dict(kind="kint", levels=16, window=8.0, flush=True),
+        dict(kind="kint", levels=4, window=3.0, interp=True, flush=True)]
+
+
+@pytest.mark.parametrize("var", VARS, ids=lambda v: "-".join(f"{k}{v[k]}" for k in v))
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_emulation_passes(var, causal):
+    r = np.random.default_rng(5)
+    N, d = 300, 64
+    q = r.standard_normal((N, d)) * 1.5
+    k = r.standard_normal((N, d)) * 1.5
+    v = r.standard_normal((N, d))
+    O, idx = emulate(var, q, k, v, causal)
+    rep, _ = parity.compare_head(var, q, k, v, np.arange(N), O, idx, causal=causal, tol=1e-4)
+    assert rep.idx_bad == 0
+    if not var.get("interp"):
+        assert rep.idx_agree >= 0.999
+
+
+def test_wrong_index_outside_band_fails():
+    r = np.random.default_rng(6)
+    N, d = 128, 64
+    q, k, v = r.standard_normal((N, d)) * 1.5, r.standard_normal((N, d)) * 1.5, r.standard_normal((N, d))
+    var = dict(kind="pot", levels=8)
+    O, idx = emulate(var, q, k, v, False)
+    ref_rep, ref = parity.compare_head(var, q, k, v, np.arange(N), O, idx, causal=False, tol=1e-4)
+    y = ref["y"]
+    i, j = np.unravel_index(np.argmin(np.abs(y - np.floor(y) - 0.5) * -1 + (idx == 7) * 9), y.shape)
+    bad = idx.copy()
+    bad[i, j] = (bad[i, j] + 1) % 7                               # a flip far from any edge
+    with pytest.raises(AssertionError):
+        parity.compare_head(var, q, k, v, np.arange(N), O, bad, causal=False, tol=1e-4)
+    O2 = O.copy()
+    O2[3] *= 1.05
+    with pytest.raises(AssertionError):
+        parity.compare_head(var, q, k, v, np.arange(N), O2, idx, causal=False, tol=1e-2)
