@@ -2,25 +2,31 @@
 //
 // The fused path follows the wiki summary's flowchart of the method ("QK tile
 // -> Row max (anchor point) -> Power-of-two weights -> PV matmul -> Output"),
-// built for CDNA4:
+// laid out for CDNA4:
 //
-//   * one workgroup = 4 waves = BM = 128 query rows of one (batch, head);
-//     each wave owns 32 rows for the whole kernel (Q stays in VGPRs);
-//   * scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: lane (i, h) of a wave holds query row i of its
-//     32 and 16 keys of each 32-key block, so row maxima, minima and sums are
-//     in-lane reductions plus one exchange between the two half-waves;
-//   * the accumulator layout of S^T is already the B operand of the PV
-//     product O^T = V^T P^T, so P never moves between lanes; V is transposed
-//     once on its way into LDS to match;
-//   * anchored kinds (Rowmax-PoT, K-interval, exact-anchored) first run a
-//     pre-pass over all key tiles for the true row maximum (and minimum for
-//     min-max calibration), then the main loop forms weights against that
-//     fixed anchor, so O needs no per-tile rescale.  The online exact control
-//     skips the pre-pass and rescales by 2^(m_old - m_new) when a row's
-//     running maximum grows;
-//   * K and V tiles (64 keys) are staged in LDS; the next tile's global loads
-//     are in flight while the current tile is computed.
+//   * one workgroup = 4 waves = 128 query rows of one (batch, head); each
+//     wave owns 32 rows for the whole kernel (its Q^T operand stays in VGPRs);
+//   * scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_32x32x16_bf16: lane (i, h) of a wave holds query row i and 16
+//     keys of each 32-key block, so row maxima, minima and sums are in-lane
+//     reductions plus one exchange between the two half-waves;
+//   * the accumulator layout of S^T is the B operand of O^T = V^T P^T, so P
+//     never moves between lanes; V is transposed once on its way into LDS;
+//   * anchored kinds run a pre-pass over all key tiles for the true row
+//     maximum (and minimum for min-max calibration).  The main loop then
+//     starts each score accumulation at -M (a register vector holding the
+//     row max), so the MFMA itself delivers s' = acc - M <= 0 and the weight
+//     needs no per-element subtraction; O needs no per-tile rescale;
+//   * the online exact control skips the pre-pass and rescales O by
+//     2^(m_old - m_new) when a row's running maximum grows;
+//   * K and V tiles of 64 keys are double-buffered in LDS, filled from
+//     buffer loads (hardware zero-fill past the end of the head) one tile
+//     ahead, with one workgroup barrier per tile; the scores of tile t+1 are
+//     computed on the matrix cores while the weights of tile t are formed on
+//     the VALU, so the two overlap within each wave;
+//   * only a wave's last tile can need masking (causal diagonal or the ragged
+//     end of the sequence); it runs a separate code path, so the steady-state
+//     tiles carry no mask arithmetic.
 #include "qsa_common.h"
 #include "qsa_weights.h"
 
@@ -32,13 +38,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;   // waves per workgroup
-constexpr int BN = 64;  // keys per tile
+constexpr int NW = 4;    // waves per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
 
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
 }
 
 // Round-to-nearest-even pack of two floats into two bf16 (low = a).
@@ -47,33 +56,56 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Sum of the two bf16 in `p` added to `acc` (v_dot2_f32_bf16 against 1.0).
+// acc + the two bf16 of p (v_dot2_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
 }
 
-__device__ __forceinline__ float half_swap(float x) { return __shfl_xor(x, 32, 64); }
+// max / min / sum of a value held by lane l and lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fmaxf(bitsf(r[0]), bitsf(r[1]));
+}
+__device__ __forceinline__ float half_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fminf(bitsf(r[0]), bitsf(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
 
-// Row and key of accumulator register r of lane (li, hh) in a 32x32 block.
+// Key of accumulator register r of lane half hh in a 32x32 S^T block.
 __device__ __forceinline__ int acc_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-template <int D, int WK, int QB>
+// Two bf16 weights 2^-e0, 2^-e1 (e clipped to L-1) from t = 2^24 - y (rounded).
+// The low halves of bits(t) are -e as int16; v_pk_mad_u16 turns the pair into
+// the bf16 exponent fields (127 - e) << 7 and v_pk_max_i16 applies the clip.
+__device__ __forceinline__ uint32_t pot_pair(float t0, float t1, uint32_t lo_clip) {
+  const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+  uint32_t w;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(w) : "v"(ne), "v"(0x00800080u), "v"(0x3F803F80u));
+  const s16x2 c = __builtin_elementwise_max(__builtin_bit_cast(s16x2, w), __builtin_bit_cast(s16x2, lo_clip));
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+template <int D, int WK, bool DUMP>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
-  constexpr int BM = NW * QB * 32;
   constexpr int KC = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
-  constexpr int NB = BN / 32; // 32-key blocks per tile
   constexpr int C8 = D / 8;   // 16-byte chunks per K row
+  constexpr int KR = D * 2 + 16;   // bytes of one K row in LDS (16-byte pad: conflict-free column reads)
+  constexpr int KT = BN * KR;      // bytes of one K (or V) tile buffer
+  static_assert(BN * D * 2 <= KT, "V tile fits a K-sized buffer");
   constexpr bool ANCH = (WK != WK_EXACT);
-  constexpr bool PACK_EXACT_BITS = (WK == WK_POT || WK == WK_POT_FLUSH);
-  constexpr int SH = (BM == 128) ? 9 : (BM == 256 ? 10 : 8);
-  static_assert((1 << SH) == BM * 4, "table shift");
+  constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
+  constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
+  constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
+  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* Ks = smem;
-  unsigned char* Vs = smem + BN * D * 2;
-  unsigned char* Tb = smem + 2 * BN * D * 2;
+  unsigned char* const Tb = smem + 4 * KT;  // K-interval tables
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hh = lane >> 5;
@@ -83,332 +115,380 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   const int kvh = h / (a.H / a.Hkv);
   const int N = a.N;
   const int q0 = qt * BM;
-  const int wr0 = q0 + wave * QB * 32;
+  const int wr0 = q0 + wave * 32;
+  const int row = wr0 + li;
   const __bf16* Qg = (const __bf16*)a.q + (size_t)(b * a.H + h) * N * D;
-  const __bf16* Kg = (const __bf16*)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
-  const __bf16* Vg = (const __bf16*)a.v + (size_t)(b * a.Hkv + kvh) * N * D;
+  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * N * D;
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.k + kv_off), 0,
+                                                                      N * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.v + kv_off), 0,
+                                                                      N * D * 2, 0x00020000);
 
   // Q^T operand: lane (li, hh) holds Q[row][16c + 8hh .. +7].
-  u32x4 qf[QB][KC];
+  u32x4 qf[KC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wr0 + qb * 32 + li;
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      qf[qb][c] = row < N ? *(const u32x4*)(Qg + (size_t)row * D + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
-  }
+  for (int c = 0; c < KC; ++c)
+    qf[c] = row < N ? *(const u32x4*)(Qg + (size_t)row * D + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
 
-  const int ntile_all = (N + BN - 1) / BN;
-  const int qend = min(q0 + BM, N);
-  const int kt_end = a.causal ? ((qend - 1) / BN + 1) : ntile_all;
-  const bool wave_active = wr0 < N;
-  const int wrow_last = min(wr0 + QB * 32, N) - 1;
-  const int wkt_last = a.causal ? (wrow_last / BN) : (ntile_all - 1);
+  const int T = a.causal ? ((min(q0 + BM, N) - 1) / BN + 1) : (N + BN - 1) / BN;  // tiles of this workgroup
+  // last tile this wave computes (-1: none); only that tile can need masking
+  const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
+  const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
 
-  // ---- global -> register -> LDS staging --------------------------------
-  constexpr int KU = BN * C8 / (NW * 64);
-  constexpr int VU = (BN / 4) * C8;
+  // ---- tile staging: buffer loads -> registers -> LDS ---------------------
+  // (the whole byte offset goes in the VGPR operand, which the range check covers)
+  constexpr int KU = BN * C8 / (NW * 64);  // 16-byte K chunks per thread
+  constexpr int VU = (BN / 4) * C8;        // threads that stage V (4 keys x 8 columns each)
   static_assert(KU >= 1 && VU <= NW * 64, "tile staging");
-  u32x4 kr[KU];
-  u32x4 vr[4];
+  u32x4 kr[KU], vr[4];
   auto load_k = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NW * 64, j = u / C8, c = u % C8, key = kt * BN + j;
-      kr[i] = key < N ? *(const u32x4*)(Kg + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
+      const int u = tid + i * NW * 64, j = u / C8, c = u % C8;
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rK, kt * (BN * D * 2) + (j * D + c * 8) * 2, 0, 0);
     }
   };
-  auto store_k = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
       const int u = tid + i * NW * 64, j = u / C8, c = u % C8;
-      *(u32x4*)(Ks + j * D * 2 + ((c ^ (j % C8)) * 16)) = kr[i];
+      *(u32x4*)(smem + buf * KT + j * KR + c * 16) = kr[i];
     }
   };
   auto load_v = [&](int kt) {
     if (tid < VU) {
       const int co = tid % C8, kq = tid / C8;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BN + 4 * kq + r;
-        vr[r] = key < N ? *(const u32x4*)(Vg + (size_t)key * D + co * 8) : u32x4{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r)
+        vr[r] = __builtin_amdgcn_raw_buffer_load_b128(rV, kt * (BN * D * 2) + ((4 * kq + r) * D + co * 8) * 2, 0, 0);
     }
   };
   // V^T layout: 16-byte slot (g, hb, dcol) holds V[16g + 4hb + 0..3][dcol] then
   // V[16g + 8 + 4hb + 0..3][dcol]: the keys lane half hb multiplies in k-step g.
-  auto vslot = [&](int g, int hb, int dcol) { return ((g * 2 + hb) * D + (dcol ^ ((dcol >> 3) & 7))) * 16; };
-  auto store_v = [&]() {
+  auto vslot = [](int g, int hb, int dcol) { return ((g * 2 + hb) * D + (dcol ^ ((dcol >> 3) & 7))) * 16; };
+  auto store_v = [&](int buf) {
     if (tid < VU) {
       const int co = tid % C8, kq = tid / C8;
       const int g = kq >> 2, hb = kq & 1, half = (kq >> 1) & 1;
+      unsigned char* base = smem + (2 + buf) * KT + half * 8;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const u32x2 lo = {__builtin_amdgcn_perm(vr[1][p], vr[0][p], 0x05040100u),
                           __builtin_amdgcn_perm(vr[3][p], vr[2][p], 0x05040100u)};
         const u32x2 hi = {__builtin_amdgcn_perm(vr[1][p], vr[0][p], 0x07060302u),
                           __builtin_amdgcn_perm(vr[3][p], vr[2][p], 0x07060302u)};
-        *(u32x2*)(Vs + vslot(g, hb, co * 8 + 2 * p) + half * 8) = lo;
-        *(u32x2*)(Vs + vslot(g, hb, co * 8 + 2 * p + 1) + half * 8) = hi;
+        *(u32x2*)(base + vslot(g, hb, co * 8 + 2 * p)) = lo;
+        *(u32x2*)(base + vslot(g, hb, co * 8 + 2 * p + 1)) = hi;
       }
     }
   };
-  auto rdK = [&](int kb, int c) -> u32x4 {
-    const int j = kb * 32 + li, c8 = 2 * c + hh;
-    return *(const u32x4*)(Ks + j * D * 2 + ((c8 ^ (j % C8)) * 16));
+  // A-operand read offsets (the tile buffer and the 32-key block are added as constants)
+  const uint32_t koff = li * KR + hh * 16;  // + 32 c for k-step c
+  uint32_t voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) voff[db] = vslot(0, hh, db * 32 + li);
+
+  // 32-key block kb of a tile: init + K_block Q^T  (init: the -M vector, or 0)
+  auto qk1 = [&](int buf, int kb, const f32x16& init) {
+    const unsigned char* kbase = smem + buf * KT + kb * 32 * KR + koff;
+    f32x16 s = init;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 ka = *(const u32x4*)(kbase + 32 * c);
+      s = mma(ka, qf[c], c == 0 ? init : s);
+    }
+    return s;
   };
-  auto rdV = [&](int g, int db) -> u32x4 { return *(const u32x4*)(Vs + vslot(g, hh, db * 32 + li)); };
-
-  auto qk = [&](f32x16 (&s)[QB][NB]) {
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 ka = rdK(kb, c);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mma(ka, qf[qb][c], s[qb][kb]);
-      }
-    }
+  auto qk = [&](int buf, f32x16 (&s)[2], const f32x16& init) {
+    s[0] = qk1(buf, 0, init);
+    s[1] = qk1(buf, 1, init);
   };
-  // -inf on keys a row cannot see (causal, or beyond N).
-  auto mask = [&](f32x16 (&s)[QB][NB], int kt) {
+  // O^T += V^T P^T over the 32 keys of block kb (k-steps g = 2kb, 2kb+1)
+  auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
+    const unsigned char* vbase = smem + (2 + buf) * KT;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = wr0 + qb * 32 + li;
-      const int lim = a.causal ? min(row, N - 1) : N - 1;
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * BN + kb * 32 + acc_key(r, hh);
-          s[qb][kb][r] = key <= lim ? s[qb][kb][r] : -__builtin_inff();
-        }
-    }
-  };
-  auto needs_mask = [&](int kt) { return (a.causal && kt * BN + BN - 1 > wr0) || (kt * BN + BN > N); };
-
-  // ---- pre-pass: true row extrema (anchored kinds) ------------------------
-  float M[QB], MN[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { M[qb] = -__builtin_inff(); MN[qb] = __builtin_inff(); }
-  if (ANCH) {
-    load_k(0);
-    for (int kt = 0; kt < kt_end; ++kt) {
-      __syncthreads();
-      store_k();
-      __syncthreads();
-      if (kt + 1 < kt_end) load_k(kt + 1);
-      if (wave_active && kt <= wkt_last) {
-        f32x16 s[QB][NB];
-        qk(s);
-        const bool msk = needs_mask(kt);
-        if (msk) mask(s, kt);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) M[qb] = fmaxf(M[qb], s[qb][kb][r]);
-        if (a.track_min) {
-          if (msk) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-              for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const float x = s[qb][kb][r];
-                  MN[qb] = fminf(MN[qb], x == -__builtin_inff() ? __builtin_inff() : x);
-                }
-          } else {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-              for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) MN[qb] = fminf(MN[qb], s[qb][kb][r]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      M[qb] = fmaxf(M[qb], half_swap(M[qb]));
-      MN[qb] = fminf(MN[qb], half_swap(MN[qb]));
-    }
-  }
-
-  RowC rc[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-    rc[qb] = make_row<WK, SH>(a, M[qb], MN[qb], (wave * QB + qb) * 32 + li, Tb, hh, 2);
-  // (the barrier at the top of the main loop publishes the K-interval tables)
-
-  // ---- main loop ----------------------------------------------------------
-  f32x16 o[QB][DB];
-  float l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    l[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
-  }
-  const bool dump = a.grid_idx != nullptr && wr0 < a.idx_row0 + a.idx_rows && wr0 + QB * 32 > a.idx_row0;
-
-  load_k(0);
-  load_v(0);
-  for (int kt = 0; kt < kt_end; ++kt) {
-    __syncthreads();
-    store_k();
-    store_v();
-    __syncthreads();
-    if (kt + 1 < kt_end) {
-      load_k(kt + 1);
-      load_v(kt + 1);
-    }
-    if (!(wave_active && kt <= wkt_last)) continue;
-
-    f32x16 s[QB][NB];
-    qk(s);
-    const bool msk = needs_mask(kt);
-    if (msk) mask(s, kt);
-
-    if (WK == WK_EXACT) {
-      // online softmax: grow the running max, rescale what was accumulated
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float tm = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[qb][kb][r]);
-        tm = fmaxf(tm, half_swap(tm));
-        const float mnew = fmaxf(M[qb], tm);
-        if (__ballot(mnew > M[qb])) {
-          const float alpha = (mnew > M[qb]) ? __builtin_amdgcn_exp2f((M[qb] - mnew) * rc[qb].c) : 1.0f;
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-          M[qb] = mnew;
-          rc[qb].mc = mnew * rc[qb].c;
-        }
-      }
-    }
-
-    if (dump) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int row = wr0 + qb * 32 + li;
-        if (row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
-          uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
-#pragma unroll
-          for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kt * BN + kb * 32 + acc_key(r, hh);
-              if (key < N) {
-                const float x = s[qb][kb][r];
-                dst[key] = (uint8_t)(x == -__builtin_inff() ? 255u : Weight<WK>::idx(x, rc[qb], a.levels));
-              }
-            }
-        }
-      }
-    }
-
-    // weights -> P^T operands (bf16), row sums of the weights that enter PV
-    u32x4 P[QB][2 * NB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int r0 = 8 * kc + 2 * p;
-            const float x0 = s[qb][kb][r0], x1 = s[qb][kb][r0 + 1];
-            float w0 = Weight<WK>::template w<SH>(x0, rc[qb], Tb, a.levels);
-            float w1 = Weight<WK>::template w<SH>(x1, rc[qb], Tb, a.levels);
-            if (WK != WK_EXACT && WK != WK_EXACT_ANCH && msk) {
-              w0 = x0 == -__builtin_inff() ? 0.0f : w0;
-              w1 = x1 == -__builtin_inff() ? 0.0f : w1;
-            }
-            uint32_t pk;
-            if (PACK_EXACT_BITS)  // powers of two: the bf16 pattern is the top half
-              pk = __builtin_amdgcn_perm(fbits(w1), fbits(w0), 0x07060302u);
-            else
-              pk = pack_bf16(w0, w1);
-            P[qb][2 * kb + kc][p] = pk;
-            l[qb] = dot2_ones(pk, l[qb]);
-          }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int g = 0; g < 2 * NB; ++g)
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x4 va = rdV(g, db);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mma(va, P[qb][g], o[qb][db]);
+        const u32x4 va = *(const u32x4*)(vbase + (2 * kb + kc) * 2 * D * 16 + voff[db]);
+        o[db] = mma(va, P[kc], o[db]);
       }
+  };
+  // keys up to `lim` are visible to this lane's row
+  const int lim = a.causal ? min(row, N - 1) : N - 1;
+  auto mask_fill = [&](f32x16 (&s)[2], int kt, float fill) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = (kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : fill;
+  };
+
+  // ---- pre-pass: true row extrema ------------------------------------------
+  float M = -__builtin_inff(), MN = __builtin_inff();
+  const f32x16 zero16 = {};
+  if (ANCH) {
+    const bool tmin = a.track_min;
+    load_k(0);
+    store_k(0);
+    if (T > 1) {
+      load_k(1);
+      store_k(1);
+    }
+    __syncthreads();
+    if (T > 2) load_k(2);
+    f32x16 s[2];
+    if (wlast >= 0) qk(0, s, zero16);
+    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+    for (int t = 0; t < T; ++t) {
+      if (t < wlast) {
+        f32x16 sn[2];
+        qk((t + 1) & 1, sn, zero16);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
+        if (tmin) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+        }
+        s[0] = sn[0];
+        s[1] = sn[1];
+      } else if (t == wlast) {
+        f32x16 sm[2] = {s[0], s[1]};
+        if (last_masked) mask_fill(sm, t, -__builtin_inff());
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) M = fmaxf(M, sm[kb][r]);
+        if (tmin) {
+          if (last_masked) mask_fill(s, t, __builtin_inff());
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+        }
+      }
+      if (t + 2 < T) store_k(t & 1);
+      if (t + 3 < T) load_k(t + 3);
+      __syncthreads();
+    }
+    M = half_max(M);
+    MN = half_min(MN);
+  }
+
+  RowC rc = make_row<WK, SH>(a, M, MN, wave * 32 + li, Tb, hh, 2);
+  // main-loop score accumulators start at -M: s' = acc - M
+  f32x16 init16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
+  const uint32_t pot_clip = 0x00010001u * (uint32_t)((128 - a.levels) * 128);  // (127 - (L-1)) << 7, twice
+  const int L = a.levels;
+  const float Kf = (float)a.levels;
+
+  // weights of 32-key block kb of tile kt -> 2 P^T operands (bf16) and the row sum
+  auto weights = [&](const f32x16& sb, int kb, u32x4 (&P)[2], float& l, int kt, bool masked) {
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int r0 = 8 * kc + 2 * p;
+          const float x0 = sb[r0], x1 = sb[r0 + 1];
+          uint32_t pk;
+          uint32_t i0 = 0, i1 = 0;  // grid indices (dump only)
+          if (EXACT_W) {
+            // exact: 2^((acc - M) c); the online kind folds -M c into the FMA
+            const float y0 = ANCH ? x0 * rc.c : fmaf(x0, rc.c, -rc.mc);
+            const float y1 = ANCH ? x1 * rc.c : fmaf(x1, rc.c, -rc.mc);
+            pk = pack_bf16(__builtin_amdgcn_exp2f(y0), __builtin_amdgcn_exp2f(y1));
+          } else if (POT && !FLUSH) {
+            // t = 2^24 + (acc - M) c = 2^24 - y, rounded to an integer by the FMA itself
+            const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
+            pk = pot_pair(t0, t1, pot_clip);
+            if (DUMP) {
+              i0 = 127u - ((pk >> 7) & 0x1FFu);
+              i1 = 127u - ((pk >> 23) & 0x1FFu);
+            }
+          } else if (POT) {  // flush: e >= L -> 0
+            const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
+            const int32_t lo = 0x4B800000 - (L - 1);
+            const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
+            const uint32_t w0 = b0 < lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
+            const uint32_t w1 = b1 < lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
+            pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+            if (DUMP) {
+              i0 = b0 < lo ? 254u : (uint32_t)(0x4B800000 - b0);
+              i1 = b1 < lo ? 254u : (uint32_t)(0x4B800000 - b1);
+            }
+          } else if (KHARD) {
+            // y = (M - acc) c; t = y + 2^23 rounds y: bits(t) = 0x4B000000 + l
+            const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
+            int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
+            b0 = min(max(b0, 0x4B000000), 0x4B000000 + L);
+            b1 = min(max(b1, 0x4B000000), 0x4B000000 + L);
+            float w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
+            float w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
+            const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;
+            if (FLUSH) {  // y > K: below the window
+              w0 = y0 > Kf ? 0.0f : w0;
+              w1 = y1 > Kf ? 0.0f : w1;
+            }
+            pk = pack_bf16(w0, w1);
+            if (DUMP) {
+              i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
+              i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
+            }
+          } else {  // K-interval, interpolation
+            const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
+            const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
+            const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
+            const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            const f2 e0 = *(const f2*)(Tb + ((l0 << (SH + 1)) + rc.tab));
+            const f2 e1 = *(const f2*)(Tb + ((l1 << (SH + 1)) + rc.tab));
+            float w0 = fmaf(c0 - f0, e0.y, e0.x), w1 = fmaf(c1 - f1, e1.y, e1.x);
+            if (FLUSH) {
+              w0 = y0 > Kf ? 0.0f : w0;
+              w1 = y1 > Kf ? 0.0f : w1;
+            }
+            pk = pack_bf16(w0, w1);
+            if (DUMP) {
+              i0 = (FLUSH && y0 > Kf) ? 254u : l0;
+              i1 = (FLUSH && y1 > Kf) ? 254u : l1;
+            }
+          }
+          if (masked) {
+            const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);  // r0 even: keys k0, k0 + 1
+            const uint32_t m0 = k0 <= lim ? 0x0000FFFFu : 0u, m1 = k0 + 1 <= lim ? 0xFFFF0000u : 0u;
+            pk &= (m0 | m1);
+            if (DUMP) {
+              i0 = k0 <= lim ? i0 : 255u;
+              i1 = k0 + 1 <= lim ? i1 : 255u;
+            }
+          }
+          if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+            const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);
+            uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+            if (k0 < N) dst[k0] = (uint8_t)i0;
+            if (k0 + 1 < N) dst[k0 + 1] = (uint8_t)i1;
+          }
+          P[kc][p] = pk;
+          l = dot2_ones(pk, l);
+        }
+  };
+
+  // online exact: grow the running max over this tile, rescale O and l
+  auto online_max = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l) {
+    float tm = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[kb][r]);
+    const float mnew = fmaxf(M, half_max(tm));
+    if (__builtin_amdgcn_ballot_w64(mnew > M)) {
+      const float alpha = mnew > M ? __builtin_amdgcn_exp2f((M - mnew) * rc.c) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      M = mnew;
+      rc.mc = mnew * rc.c;
+    }
+  };
+
+  // ---- main loop --------------------------------------------------------------
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float l = 0.0f;
+  __syncthreads();  // pre-pass reads done before the buffers are refilled
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (T > 1) {
+    load_k(1);
+    store_k(1);
+  }
+  __syncthreads();  // also publishes the K-interval tables
+  if (T > 2) load_k(2);
+  if (T > 1) load_v(1);
+  f32x16 s[2];
+  if (wlast >= 0) qk(0, s, init16);
+  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+  for (int t = 0; t < T; ++t) {
+    if (t < wlast) {
+      // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
+      const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+      if (WK == WK_EXACT) online_max(s, o, l);
+      u32x4 P[2];
+      weights(s[0], 0, P, l, t, false);
+      pv1(t & 1, 0, P, o);
+      const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
+      weights(s[1], 1, P, l, t, false);
+      pv1(t & 1, 1, P, o);
+      s[0] = sn0;
+      s[1] = sn1;
+    } else if (t == wlast) {
+      if (WK == WK_EXACT) {
+        f32x16 sm[2] = {s[0], s[1]};
+        if (last_masked) mask_fill(sm, t, -__builtin_inff());
+        online_max(sm, o, l);
+      }
+      u32x4 P[2];
+      weights(s[0], 0, P, l, t, last_masked);
+      pv1(t & 1, 0, P, o);
+      weights(s[1], 1, P, l, t, last_masked);
+      pv1(t & 1, 1, P, o);
+    }
+    if (t + 2 < T) store_k(t & 1);
+    if (t + 1 < T) store_v((t + 1) & 1);
+    if (t + 3 < T) load_k(t + 3);
+    if (t + 2 < T) load_v(t + 2);
+    __syncthreads();
   }
 
   // ---- epilogue -----------------------------------------------------------
-  if (!wave_active) return;
-  if (dump) {  // keys past this wave's last tile are invisible to all its rows (causal)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = wr0 + qb * 32 + li;
-      if (row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
-        uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
-        for (int key = (wkt_last + 1) * BN + hh; key < N; key += 2) dst[key] = 255u;
-      }
-    }
+  if (wlast < 0) return;
+  const float lt = half_sum(l);
+  if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+    uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+    for (int key = (wlast + 1) * BN + hh; key < N; key += 2) dst[key] = 255u;  // beyond the wave's last tile
   }
+  if (row >= N) return;
   __bf16* Og = (__bf16*)a.o + (size_t)(b * a.H + h) * N * D;
+  const float inv = a.vd / lt;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + half_swap(l[qb]);
-    const int row = wr0 + qb * 32 + li;
-    if (row >= N) continue;
-    const float inv = a.vd / lt;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dcol = db * 32 + 8 * g4 + 4 * hh;
-        const u32x2 v = {pack_bf16(o[qb][db][4 * g4 + 0] * inv, o[qb][db][4 * g4 + 1] * inv),
-                         pack_bf16(o[qb][db][4 * g4 + 2] * inv, o[qb][db][4 * g4 + 3] * inv)};
-        *(u32x2*)(Og + (size_t)row * D + dcol) = v;
-      }
-    if (hh == 0) {
-      const size_t ri = (size_t)bh * N + row;
-      if (a.row_max) a.row_max[ri] = M[qb] * a.sc;
-      if (a.row_sum) a.row_sum[ri] = lt;
-      if (a.row_lo) {
-        const bool kint = WK >= WK_KH;
-        a.row_lo[ri] = (kint && a.window_calib) ? M[qb] * a.sc - a.window : MN[qb] * a.sc;
-      }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int dcol = db * 32 + 8 * g4 + 4 * hh;
+      const u32x2 v = {pack_bf16(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv),
+                       pack_bf16(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+      *(u32x2*)(Og + (size_t)row * D + dcol) = v;
     }
+  if (hh == 0) {
+    const size_t ri = (size_t)bh * N + row;
+    if (a.row_max) a.row_max[ri] = M * a.sc;
+    if (a.row_sum) a.row_sum[ri] = lt;
+    if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
   }
 }
 
 template <int D, int WK>
 hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
-  constexpr int QB = 1;
-  constexpr int BM = NW * QB * 32;
   FwdArgs a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.total_blocks = a.B * a.H * a.n_qtiles;
-  const size_t lds = 2 * (size_t)BN * D * 2 + table_bytes(WK, BM, a.levels);
-  auto kern = fwd_bf16<D, WK, QB>;
+  const size_t lds = 4 * (size_t)BN * (D * 2 + 16) + table_bytes(WK, BM, a.levels);
+  const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true> : (const void*)fwd_bf16<D, WK, false>;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+  if (a.grid_idx)
+    hipLaunchKernelGGL((fwd_bf16<D, WK, true>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16<D, WK, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
