@@ -39,8 +39,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, objdir: str = OBJDIR) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -50,30 +50,35 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int | None = None, extra=(), verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(jobs: int | None = None, extra=(), verbose: bool = False, out: str | None = None) -> str:
+    objdir = OBJDIR if out is None else os.path.join(OBJDIR, os.path.basename(out) + ".d")
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra), objdir), srcs))
+    lib = LIB if out is None else out
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--save-temps", action="store_true", help="keep the gfx950 assembly under _build/")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor define")
+    ap.add_argument("--out", default=None, help="library path (default: the package's libqsa.so)")
     args = ap.parse_args(argv)
     extra = ["-save-temps=obj"] if args.save_temps else []
-    build(args.jobs, extra, verbose=True)
+    extra += [f"-D{d}" for d in args.defines]
+    build(args.jobs, extra, verbose=True, out=args.out)
 
 
 if __name__ == "__main__":

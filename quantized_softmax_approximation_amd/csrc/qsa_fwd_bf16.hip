@@ -11,7 +11,7 @@
 //     keys of each 32-key block, so row maxima, minima and sums are in-lane
 //     reductions plus one exchange between the two half-waves;
 //   * the accumulator layout of S^T is the B operand of O^T = V^T P^T, so P
-//     never moves between lanes; V is transposed once on its way into LDS;
+//     never moves between lanes;
 //   * anchored kinds run a pre-pass over all key tiles for the true row
 //     maximum (and minimum for min-max calibration).  The main loop then
 //     starts each score accumulation at -M (a register vector holding the
@@ -19,11 +19,14 @@
 //     needs no per-element subtraction; O needs no per-tile rescale;
 //   * the online exact control skips the pre-pass and rescales O by
 //     2^(m_old - m_new) when a row's running maximum grows;
-//   * K and V tiles of 64 keys are double-buffered in LDS, filled from
-//     buffer loads (hardware zero-fill past the end of the head) one tile
-//     ahead, with one workgroup barrier per tile; the scores of tile t+1 are
-//     computed on the matrix cores while the weights of tile t are formed on
-//     the VALU, so the two overlap within each wave;
+//   * K and V tiles of 64 keys are double-buffered in LDS and filled by
+//     buffer loads that write LDS directly (no staging registers; hardware
+//     zero-fill past the end of the head), one tile ahead, with one workgroup
+//     barrier per tile.  K rows are padded to an odd number of 16-byte slots
+//     so a column read by 16 lanes hits 16 different banks; V stays row-major
+//     and the V^T operand comes from transposing LDS reads (ds_read_b64_tr_b16);
+//   * the scores of tile t+1 are computed on the matrix cores while the
+//     weights of tile t are formed on the VALU, so the two overlap in a wave;
 //   * only a wave's last tile can need masking (causal diagonal or the ragged
 //     end of the sequence); it runs a separate code path, so the steady-state
 //     tiles carry no mask arithmetic.
@@ -39,11 +42,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int NW = 4;    // waves per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
+#ifndef QSA_BF16_WAVES_PER_SIMD
+#define QSA_BF16_WAVES_PER_SIMD 2
+#endif
 
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -91,13 +100,17 @@ __device__ __forceinline__ uint32_t pot_pair(float t0, float t1, uint32_t lo_cli
 }
 
 template <int D, int WK, bool DUMP>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
   constexpr int C8 = D / 8;   // 16-byte chunks per K row
-  constexpr int KR = D * 2 + 16;   // bytes of one K row in LDS (16-byte pad: conflict-free column reads)
-  constexpr int KT = BN * KR;      // bytes of one K (or V) tile buffer
-  static_assert(BN * D * 2 <= KT, "V tile fits a K-sized buffer");
+  constexpr int SK = D / 8 + 1;    // 16-byte slots per K row in LDS (odd: 16 rows -> 16 bank groups)
+  constexpr int SV = D / 8 + 4;    // slots per V row (row stride = 64 mod 256 bytes)
+  constexpr int KR = SK * 16, VR = SV * 16;
+  constexpr int KT = BN * KR, VT = BN * VR;  // bytes of one K / V tile buffer
+  constexpr int KIW = (SK + NW - 1) / NW;    // direct-load instructions per wave per K tile (max)
+  constexpr int VIW = (SV + NW - 1) / NW;
   constexpr bool ANCH = (WK != WK_EXACT);
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
   constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
@@ -105,7 +118,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* const Tb = smem + 4 * KT;  // K-interval tables
+  unsigned char* const Tb = smem + 2 * KT + 2 * VT;  // K-interval tables
+  lds_u8* const lds = (lds_u8*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hh = lane >> 5;
@@ -119,10 +133,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   const int row = wr0 + li;
   const __bf16* Qg = (const __bf16*)a.q + (size_t)(b * a.H + h) * N * D;
   const size_t kv_off = (size_t)(b * a.Hkv + kvh) * N * D;
-  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.k + kv_off), 0,
-                                                                      N * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)((const __bf16*)a.v + kv_off), 0,
-                                                                      N * D * 2, 0x00020000);
+  const __bf16* const Kg = (const __bf16*)a.k + kv_off;
+  const __bf16* const Vg = (const __bf16*)a.v + kv_off;
 
   // Q^T operand: lane (li, hh) holds Q[row][16c + 8hh .. +7].
   u32x4 qf[KC];
@@ -135,66 +147,57 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
   const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
 
-  // ---- tile staging: buffer loads -> registers -> LDS ---------------------
-  // (the whole byte offset goes in the VGPR operand, which the range check covers)
-  constexpr int KU = BN * C8 / (NW * 64);  // 16-byte K chunks per thread
-  constexpr int VU = (BN / 4) * C8;        // threads that stage V (4 keys x 8 columns each)
-  static_assert(KU >= 1 && VU <= NW * 64, "tile staging");
-  u32x4 kr[KU], vr[4];
-  auto load_k = [&](int kt) {
+  // ---- tile staging: buffer loads straight into LDS ------------------------
+  // A wave-instruction writes 64 consecutive 16-byte slots; slot s of a tile
+  // is row s / SK, chunk s % SK of the padded layout (pad chunks load zeros
+  // from an out-of-range offset).  The per-tile buffer resource starts at the
+  // tile and ends at the end of the head, so rows past N read as zero.
+  uint32_t kvo[KIW], vvo[VIW];
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NW * 64, j = u / C8, c = u % C8;
-      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rK, kt * (BN * D * 2) + (j * D + c * 8) * 2, 0, 0);
-    }
-  };
-  auto store_k = [&](int buf) {
+  for (int m = 0; m < KIW; ++m) {
+    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK, c = sl % SK;
+    kvo[m] = c < D / 8 ? (uint32_t)(j * D + c * 8) * 2 : 0x7FFFFFF0u;
+  }
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + i * NW * 64, j = u / C8, c = u % C8;
-      *(u32x4*)(smem + buf * KT + j * KR + c * 16) = kr[i];
-    }
+  for (int m = 0; m < VIW; ++m) {
+    const int sl = (wave + NW * m) * 64 + lane, j = sl / SV, c = sl % SV;
+    vvo[m] = c < D / 8 ? (uint32_t)(j * D + c * 8) * 2 : 0x7FFFFFF0u;
+  }
+  auto tile_rsrc = [&](const __bf16* base, int kt) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D * 2,
+                                             0x00020000);
   };
-  auto load_v = [&](int kt) {
-    if (tid < VU) {
-      const int co = tid % C8, kq = tid / C8;
+  auto load_k = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kg, kt);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[r] = __builtin_amdgcn_raw_buffer_load_b128(rV, kt * (BN * D * 2) + ((4 * kq + r) * D + co * 8) * 2, 0, 0);
-    }
+    for (int m = 0; m < KIW; ++m)
+      if (wave + NW * m < SK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + NW * m) * 1024), 16,
+                                                 kvo[m], 0, 0, 0);
   };
-  // V^T layout: 16-byte slot (g, hb, dcol) holds V[16g + 4hb + 0..3][dcol] then
-  // V[16g + 8 + 4hb + 0..3][dcol]: the keys lane half hb multiplies in k-step g.
-  auto vslot = [](int g, int hb, int dcol) { return ((g * 2 + hb) * D + (dcol ^ ((dcol >> 3) & 7))) * 16; };
-  auto store_v = [&](int buf) {
-    if (tid < VU) {
-      const int co = tid % C8, kq = tid / C8;
-      const int g = kq >> 2, hb = kq & 1, half = (kq >> 1) & 1;
-      unsigned char* base = smem + (2 + buf) * KT + half * 8;
+  auto load_v = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const u32x2 lo = {__builtin_amdgcn_perm(vr[1][p], vr[0][p], 0x05040100u),
-                          __builtin_amdgcn_perm(vr[3][p], vr[2][p], 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(vr[1][p], vr[0][p], 0x07060302u),
-                          __builtin_amdgcn_perm(vr[3][p], vr[2][p], 0x07060302u)};
-        *(u32x2*)(base + vslot(g, hb, co * 8 + 2 * p)) = lo;
-        *(u32x2*)(base + vslot(g, hb, co * 8 + 2 * p + 1)) = hi;
-      }
-    }
+    for (int m = 0; m < VIW; ++m)
+      if (wave + NW * m < SV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + 2 * KT + buf * VT + (wave + NW * m) * 1024), 16, vvo[m], 0, 0, 0);
   };
+  // this wave's LDS-direct loads have landed (before the workgroup barrier)
+  auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // A-operand read offsets (the tile buffer and the 32-key block are added as constants)
   const uint32_t koff = li * KR + hh * 16;  // + 32 c for k-step c
-  uint32_t voff[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) voff[db] = vslot(0, hh, db * 32 + li);
+  // V^T operand: in each 16-lane group, lane 4q + p points at V[key q][4p .. 4p+3] of the
+  // group's 16 columns; the transposing read hands lane l column l and keys q = 0..3.
+  const uint32_t vtr = (4 * hh + ((lane & 15) >> 2)) * VR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   // 32-key block kb of a tile: init + K_block Q^T  (init: the -M vector, or 0)
   auto qk1 = [&](int buf, int kb, const f32x16& init) {
-    const unsigned char* kbase = smem + buf * KT + kb * 32 * KR + koff;
+    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
     f32x16 s = init;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *(const u32x4*)(kbase + 32 * c);
+      const u32x4 ka = *(const __attribute__((address_space(3))) u32x4*)(kbase + 32 * c);
       s = mma(ka, qf[c], c == 0 ? init : s);
     }
     return s;
@@ -205,12 +208,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   };
   // O^T += V^T P^T over the 32 keys of block kb (k-steps g = 2kb, 2kb+1)
   auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
-    const unsigned char* vbase = smem + (2 + buf) * KT;
+    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x4 va = *(const u32x4*)(vbase + (2 * kb + kc) * 2 * D * 16 + voff[db]);
+        const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * VR + 64 * db;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * VR));
+        const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
         o[db] = mma(va, P[kc], o[db]);
       }
   };
@@ -228,18 +235,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   const f32x16 zero16 = {};
   if (ANCH) {
     const bool tmin = a.track_min;
-    load_k(0);
-    store_k(0);
-    if (T > 1) {
-      load_k(1);
-      store_k(1);
-    }
+    load_k(0, 0);
+    if (T > 1) load_k(1, 1);
+    loads_done();
     __syncthreads();
-    if (T > 2) load_k(2);
     f32x16 s[2];
     if (wlast >= 0) qk(0, s, zero16);
     __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
     for (int t = 0; t < T; ++t) {
+      if (t + 2 < T) load_k(t + 2, t & 1);  // buffer t&1 was last read in iteration t-1
       if (t < wlast) {
         f32x16 sn[2];
         qk((t + 1) & 1, sn, zero16);
@@ -270,8 +274,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
             for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
         }
       }
-      if (t + 2 < T) store_k(t & 1);
-      if (t + 3 < T) load_k(t + 3);
+      loads_done();
       __syncthreads();
     }
     M = half_max(M);
@@ -401,21 +404,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float l = 0.0f;
   __syncthreads();  // pre-pass reads done before the buffers are refilled
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if (T > 1) {
-    load_k(1);
-    store_k(1);
-  }
+  load_k(0, 0);
+  load_v(0, 0);
+  if (T > 1) load_k(1, 1);
+  loads_done();
   __syncthreads();  // also publishes the K-interval tables
-  if (T > 2) load_k(2);
-  if (T > 1) load_v(1);
   f32x16 s[2];
   if (wlast >= 0) qk(0, s, init16);
   __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
   for (int t = 0; t < T; ++t) {
+    if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
+    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
     if (t < wlast) {
       // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
       const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
@@ -440,10 +439,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
       weights(s[1], 1, P, l, t, last_masked);
       pv1(t & 1, 1, P, o);
     }
-    if (t + 2 < T) store_k(t & 1);
-    if (t + 1 < T) store_v((t + 1) & 1);
-    if (t + 3 < T) load_k(t + 3);
-    if (t + 2 < T) load_v(t + 2);
+    loads_done();
     __syncthreads();
   }
 
@@ -472,6 +468,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
     if (a.row_sum) a.row_sum[ri] = lt;
     if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
   }
+#endif
 }
 
 template <int D, int WK>
@@ -479,7 +476,7 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   FwdArgs a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.total_blocks = a.B * a.H * a.n_qtiles;
-  const size_t lds = 4 * (size_t)BN * (D * 2 + 16) + table_bytes(WK, BM, a.levels);
+  const size_t lds = 2 * (size_t)BN * ((D / 8 + 1) + (D / 8 + 4)) * 16 + table_bytes(WK, BM, a.levels);
   const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true> : (const void*)fwd_bf16<D, WK, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

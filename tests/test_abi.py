@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     names = re.findall(r"^\s*(?:int|const char\*)\s+(qsa_\w+)\s*\(", src, flags=re.M)
     assert set(names) == {"qsa_attn_fwd", "qsa_attn_fwd_ex", "qsa_attn_validate", "qsa_status_string",
                           "qsa_last_error", "qsa_version"}
-    L = ctypes.CDLL(qsa.lib_path())
+    L = ctypes.CDLL(qsa.lib_path(), mode=os.RTLD_NOW | os.RTLD_LOCAL)  # every symbol resolves at load
     for n in names:
         assert hasattr(L, n), n
 
