@@ -145,7 +145,7 @@ int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, int B,
   switch (dtype) {
     case QSA_DT_F32: e = qsa::launch_f32(a, d, wk, s); break;
     case QSA_DT_BF16: e = qsa::launch_bf16(a, d, wk, s); break;
-    default: return fail(QSA_ERR_UNSUPPORTED, "fp8 e4m3 inputs are not built yet");
+    default: e = qsa::launch_fp8(a, d, wk, s); break;
   }
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

@@ -1,0 +1,569 @@
+// Fused quantized-softmax attention forward, OCP fp8 e4m3 Q/K/V with
+// per-tensor descales (O in bf16), gfx950 MFMA.
+//
+// Same structure as the bf16 kernel (one workgroup = 4 waves = 128 query rows;
+// S^T = K Q^T so a lane owns a query row; true-row-max pre-pass; main-loop
+// accumulators start at -M; double-buffered LDS tiles with one barrier per
+// tile; masking only on a wave's last tile), with the score product on the
+// 8-bit matrix cores: v_mfma_f32_32x32x64_f8f6f4, 64 key-or-feature columns
+// per instruction.
+//
+// The PV product depends on whether the weights fit an 8-bit float exactly:
+//   * Rowmax-PoT: the weights 2^-e ("Approximating Softmax in Pretrained
+//     LLMs", abstract: power-of-two weights anchored at each row maximum) are
+//     exact in bf8 e5m2 as 2^(1-e), e <= 15, so P^T is built directly as bf8
+//     bytes from the exponent and PV runs on the 8-bit matrix cores with V in
+//     e4m3 (operand formats e4m3 x bf8).  The V^T operand comes from 8-bit
+//     transposing LDS reads (ds_read_b64_tr_b8).
+//   * exact and K-interval weights are not representable in 8 bits without
+//     rounding errors of a few percent per row (e4m3 keeps 3 mantissa bits),
+//     so their PV runs in bf16: V tiles are widened e4m3 -> bf16 (exactly)
+//     while they are staged into LDS and P^T is bf16, as in the bf16 kernel.
+#include "qsa_common.h"
+#include "qsa_mfma_util.h"
+#include "qsa_weights.h"
+
+namespace qsa {
+namespace {
+
+constexpr int NW = 4;    // waves per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
+
+// Two PoT weights from t = 2^24 - y (rounded): the clipped exponent pair
+// u = (-e0, -e1) as int16 gives both the bf8 bytes of 2^(1-e) (low byte of each
+// 16-bit half) and the bf16 patterns of the same 2^(1-e) for the row sum.
+__device__ __forceinline__ void pot8_pair(float t0, float t1, uint32_t clip, uint32_t& b8, uint32_t& b16) {
+  const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+  const s16x2 u = __builtin_elementwise_max(__builtin_bit_cast(s16x2, ne), __builtin_bit_cast(s16x2, clip));
+  const uint32_t uu = __builtin_bit_cast(uint32_t, u);
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(b8) : "v"(uu), "v"(0x00040004u), "v"(0x00400040u));   // (16 - e) << 2
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(b16) : "v"(uu), "v"(0x00800080u), "v"(0x40004000u));  // (128 - e) << 7
+}
+
+template <int D, int WK, bool DUMP>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
+  constexpr int KC = D / 64;  // k-steps of the QK product
+  constexpr int DB = D / 32;  // 32-column blocks of O^T
+  constexpr bool ANCH = (WK != WK_EXACT);
+  constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
+  constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
+  constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
+  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
+  constexpr bool PV8 = POT;
+  constexpr int SK = D / 16 + 1;                      // 16-byte slots per K row (odd)
+  constexpr int SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);  // fp8 V rows, or bf16 rows (stride 64 mod 256)
+  constexpr int KR = SK * 16, VR = SV * 16;
+  constexpr int KT = BN * KR, VT = BN * VR;
+  constexpr int KIW = (SK + NW - 1) / NW;
+  constexpr int VIW = (SV + NW - 1) / NW;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* const Tb = smem + 2 * KT + 2 * VT;  // K-interval tables
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+  int bh, qt;
+  map_block(a, bh, qt);
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int kvh = h / (a.H / a.Hkv);
+  const int N = a.N;
+  const int q0 = qt * BM;
+  const int wr0 = q0 + wave * 32;
+  const int row = wr0 + li;
+  const uint8_t* Qg = (const uint8_t*)a.q + (size_t)(b * a.H + h) * N * D;
+  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * N * D;
+  const uint8_t* const Kg = (const uint8_t*)a.k + kv_off;
+  const uint8_t* const Vg = (const uint8_t*)a.v + kv_off;
+
+  // Q^T operand: lane (li, hh) holds Q[row][64c + 32hh .. +31].
+  i32x8 qf[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    if (row < N) {
+      lo = *(const u32x4*)(Qg + (size_t)row * D + 64 * c + 32 * hh);
+      hi = *(const u32x4*)(Qg + (size_t)row * D + 64 * c + 32 * hh + 16);
+    }
+    qf[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  const int T = a.causal ? ((min(q0 + BM, N) - 1) / BN + 1) : (N + BN - 1) / BN;
+  const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
+  const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
+
+  // ---- tile staging ------------------------------------------------------
+  // K (and V for PoT): buffer loads straight into LDS, 64 consecutive 16-byte
+  // slots per wave-instruction; slot s is row s / S, chunk s % S (pad chunks
+  // load zeros from an out-of-range offset).
+  uint32_t kvo[KIW];
+#pragma unroll
+  for (int m = 0; m < KIW; ++m) {
+    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK, c = sl % SK;
+    kvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+  }
+  auto tile_rsrc = [&](const uint8_t* base, int kt) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D, 0x00020000);
+  };
+  auto load_k = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kg, kt);
+#pragma unroll
+    for (int m = 0; m < KIW; ++m)
+      if (wave + NW * m < SK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
+  };
+  uint32_t vvo[PV8 ? VIW : 1];
+  if (PV8) {
+#pragma unroll
+    for (int m = 0; m < VIW; ++m) {
+      const int sl = (wave + NW * m) * 64 + lane, j = sl / SV, c = sl % SV;
+      vvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+    }
+  }
+  // bf16-PV kinds: each thread widens a quarter row of V (D/4 fp8 -> bf16) into LDS
+  constexpr int VQ = D / 4;        // bytes of V a thread stages
+  constexpr int VQL = VQ / 16;     // 16-byte loads per thread
+  u32x4 vst[PV8 ? 1 : VQL];
+  const int vrow = tid >> 2, vpart = tid & 3;
+  auto load_v = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
+    if (PV8) {
+#pragma unroll
+      for (int m = 0; m < VIW; ++m)
+        if (wave + NW * m < SV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, (__attribute__((address_space(3))) void*)(lds + 2 * KT + buf * VT + (wave + NW * m) * 1024), 16,
+              vvo[m], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < VQL; ++m)
+        vst[m] = __builtin_amdgcn_raw_buffer_load_b128(r, vrow * D + vpart * VQ + 16 * m, 0, 0);
+    }
+  };
+  auto store_v = [&](int buf) {  // bf16-PV kinds: widen the staged quarter row into the bf16 tile
+    if (!PV8) {
+      lds_u8* dst = lds + 2 * KT + buf * VT + vrow * VR + vpart * VQ * 2;
+#pragma unroll
+      for (int m = 0; m < VQL; ++m) {
+        u32x4 w0, w1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = vst[m][q];
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+          if (q < 2) {
+            w0[2 * q] = __builtin_bit_cast(uint32_t, lo);
+            w0[2 * q + 1] = __builtin_bit_cast(uint32_t, hi);
+          } else {
+            w1[2 * q - 4] = __builtin_bit_cast(uint32_t, lo);
+            w1[2 * q - 3] = __builtin_bit_cast(uint32_t, hi);
+          }
+        }
+        *(lds_u32x4*)(dst + 32 * m) = w0;
+        *(lds_u32x4*)(dst + 32 * m + 16) = w1;
+      }
+    }
+  };
+  auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // QK operand reads: lane (li, hh), k-step c: 32 bytes of K row li at 64c + 32hh
+  const uint32_t koff = li * KR + hh * 32;
+  auto qk1 = [&](int buf, int kb, const f32x16& init) {
+    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
+    f32x16 s = init;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 lo = *(const lds_u32x4*)(kbase + 64 * c);
+      const u32x4 hi = *(const lds_u32x4*)(kbase + 64 * c + 16);
+      const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      s = mma8<0>(ka, qf[c], c == 0 ? init : s);
+    }
+    return s;
+  };
+  auto qk = [&](int buf, f32x16 (&s)[2], const f32x16& init) {
+    s[0] = qk1(buf, 0, init);
+    s[1] = qk1(buf, 1, init);
+  };
+  // bf16 PV (exact / K-interval): V^T operand via 16-bit transposing reads of the bf16 tile
+  const uint32_t vtr16 = (4 * hh + ((lane & 15) >> 2)) * VR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
+    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr16;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * VR + 64 * db;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * VR));
+        const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+        o[db] = mma(va, P[kc], o[db]);
+      }
+  };
+  // fp8 PV (PoT): byte e of the P^T operand is key 16(e/8) + 8((e/4)%2) + 4hh + e%4 of the tile
+  // (accumulator register e%16 of block e/16); 8-bit transposing reads put V[that key][dcol]
+  // in byte e of lane (dcol, hh): in each 16-lane group, lane 2q + p points at
+  // V[row q][8p .. 8p+7] of the group's 16 columns, row q = key 4hh + q%4 + 8(q/4) (+16 per read).
+  const uint32_t vtr8 = (4 * hh + (((lane & 15) >> 1) & 3) + 8 * ((lane & 15) >> 3)) * VR +
+                        16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB]) {
+    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr8;
+    const i32x8 pb = {(int)P8[0], (int)P8[1], (int)P8[2], (int)P8[3], (int)P8[4], (int)P8[5], (int)P8[6], (int)P8[7]};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      i32x8 va;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vbase + 16 * k * VR + 32 * db));
+        va[2 * k] = v2[0];
+        va[2 * k + 1] = v2[1];
+      }
+      o[db] = mma8<1>(va, pb, o[db]);
+    }
+  };
+  const int lim = a.causal ? min(row, N - 1) : N - 1;
+  auto mask_fill = [&](f32x16 (&s)[2], int kt, float fill) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = (kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : fill;
+  };
+
+  // ---- pre-pass: true row extrema ------------------------------------------
+  float M = -__builtin_inff(), MN = __builtin_inff();
+  const f32x16 zero16 = {};
+  if (ANCH) {
+    const bool tmin = a.track_min;
+    load_k(0, 0);
+    if (T > 1) load_k(1, 1);
+    loads_done();
+    __syncthreads();
+    f32x16 s[2];
+    if (wlast >= 0) qk(0, s, zero16);
+    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+    for (int t = 0; t < T; ++t) {
+      if (t + 2 < T) load_k(t + 2, t & 1);
+      if (t < wlast) {
+        f32x16 sn[2];
+        qk((t + 1) & 1, sn, zero16);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
+        if (tmin) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+        }
+        s[0] = sn[0];
+        s[1] = sn[1];
+      } else if (t == wlast) {
+        f32x16 sm[2] = {s[0], s[1]};
+        if (last_masked) mask_fill(sm, t, -__builtin_inff());
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) M = fmaxf(M, sm[kb][r]);
+        if (tmin) {
+          if (last_masked) mask_fill(s, t, __builtin_inff());
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+        }
+      }
+      loads_done();
+      __syncthreads();
+    }
+    M = half_max(M);
+    MN = half_min(MN);
+  }
+
+  RowC rc = make_row<WK, SH>(a, M, MN, wave * 32 + li, Tb, hh, 2);
+  f32x16 init16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
+  const uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(1 - a.levels);  // -(L-1), twice
+  const int L = a.levels;
+  const float Kf = (float)a.levels;
+
+  // bf16 weights of 32-key block kb (exact / K-interval), as in the bf16 kernel
+  auto weights16 = [&](const f32x16& sb, int kb, u32x4 (&P)[2], float& l, int kt, bool masked) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r0 = 8 * kc + 2 * p;
+        const float x0 = sb[r0], x1 = sb[r0 + 1];
+        uint32_t pk;
+        uint32_t i0 = 0, i1 = 0;
+        if (EXACT_W) {
+          const float y0 = ANCH ? x0 * rc.c : fmaf(x0, rc.c, -rc.mc);
+          const float y1 = ANCH ? x1 * rc.c : fmaf(x1, rc.c, -rc.mc);
+          pk = pack_bf16(__builtin_amdgcn_exp2f(y0), __builtin_amdgcn_exp2f(y1));
+        } else if (KHARD) {
+          const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
+          int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
+          b0 = min(max(b0, 0x4B000000), 0x4B000000 + L);
+          b1 = min(max(b1, 0x4B000000), 0x4B000000 + L);
+          float w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
+          float w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
+          const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;
+          if (FLUSH) {
+            w0 = y0 > Kf ? 0.0f : w0;
+            w1 = y1 > Kf ? 0.0f : w1;
+          }
+          pk = pack_bf16(w0, w1);
+          if (DUMP) {
+            i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
+            i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
+          }
+        } else {  // K-interval, interpolation
+          const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
+          const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
+          const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
+          const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          const f2 e0 = *(const f2*)(Tb + ((l0 << (SH + 1)) + rc.tab));
+          const f2 e1 = *(const f2*)(Tb + ((l1 << (SH + 1)) + rc.tab));
+          float w0 = fmaf(c0 - f0, e0.y, e0.x), w1 = fmaf(c1 - f1, e1.y, e1.x);
+          if (FLUSH) {
+            w0 = y0 > Kf ? 0.0f : w0;
+            w1 = y1 > Kf ? 0.0f : w1;
+          }
+          pk = pack_bf16(w0, w1);
+          if (DUMP) {
+            i0 = (FLUSH && y0 > Kf) ? 254u : l0;
+            i1 = (FLUSH && y1 > Kf) ? 254u : l1;
+          }
+        }
+        const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);
+        if (masked) {
+          const uint32_t m0 = k0 <= lim ? 0x0000FFFFu : 0u, m1 = k0 + 1 <= lim ? 0xFFFF0000u : 0u;
+          pk &= (m0 | m1);
+          if (DUMP) {
+            i0 = k0 <= lim ? i0 : 255u;
+            i1 = k0 + 1 <= lim ? i1 : 255u;
+          }
+        }
+        if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+          uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+          if (k0 < N) dst[k0] = (uint8_t)i0;
+          if (k0 + 1 < N) dst[k0 + 1] = (uint8_t)i1;
+        }
+        P[kc][p] = pk;
+        l = dot2_ones(pk, l);
+      }
+  };
+
+  // PoT weights of a whole 64-key tile as bf8 bytes (P8) + row sum of the same 2^(1-e)
+  auto weights8 = [&](const f32x16 (&s)[2], uint32_t (&P8)[8], float& l, int kt, bool masked) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r0 = 4 * (w & 3);
+      uint32_t b8[2];
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        const int r = r0 + 2 * hp;
+        const float t0 = fmaf(s[kb][r], rc.c, 16777216.0f), t1 = fmaf(s[kb][r + 1], rc.c, 16777216.0f);
+        uint32_t bb, b16;
+        uint32_t i0 = 0, i1 = 0;
+        if (!FLUSH) {
+          pot8_pair(t0, t1, pot_clip, bb, b16);
+          if (DUMP) {
+            const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+            const s16x2 u = __builtin_elementwise_max(__builtin_bit_cast(s16x2, ne), __builtin_bit_cast(s16x2, pot_clip));
+            i0 = (uint32_t)(-(int)u[0]);
+            i1 = (uint32_t)(-(int)u[1]);
+          }
+        } else {  // e >= L -> 0
+          const int32_t lo = 0x4B800000 - (L - 1);
+          const int32_t c0 = (int32_t)fbits(t0), c1 = (int32_t)fbits(t1);
+          const uint32_t e0 = (uint32_t)(0x4B800000 - c0), e1 = (uint32_t)(0x4B800000 - c1);
+          const uint32_t k0 = c0 < lo ? 0u : 0xFFFFu, k1 = c1 < lo ? 0u : 0xFFFFu;
+          const uint32_t e0c = c0 < lo ? 0u : e0, e1c = c1 < lo ? 0u : e1;
+          bb = (((16u - e0c) << 2) & k0) | ((((16u - e1c) << 2) & k1) << 16);
+          b16 = (((128u - e0c) << 7) & k0) | ((((128u - e1c) << 7) & k1) << 16);
+          if (DUMP) {
+            i0 = c0 < lo ? 254u : e0;
+            i1 = c1 < lo ? 254u : e1;
+          }
+        }
+        const int key0 = kt * BN + kb * 32 + acc_key(r, hh);
+        if (masked) {
+          const uint32_t m = (key0 <= lim ? 0x0000FFFFu : 0u) | (key0 + 1 <= lim ? 0xFFFF0000u : 0u);
+          bb &= m;
+          b16 &= m;
+          if (DUMP) {
+            i0 = key0 <= lim ? i0 : 255u;
+            i1 = key0 + 1 <= lim ? i1 : 255u;
+          }
+        }
+        if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+          uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+          if (key0 < N) dst[key0] = (uint8_t)i0;
+          if (key0 + 1 < N) dst[key0 + 1] = (uint8_t)i1;
+        }
+        b8[hp] = bb;
+        l = dot2_ones(b16, l);
+      }
+      P8[w] = __builtin_amdgcn_perm(b8[1], b8[0], 0x06040200u);  // low bytes of the four halves
+    }
+  };
+
+  auto online_max = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l) {
+    float tm = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[kb][r]);
+    const float mnew = fmaxf(M, half_max(tm));
+    if (__builtin_amdgcn_ballot_w64(mnew > M)) {
+      const float alpha = mnew > M ? __builtin_amdgcn_exp2f((M - mnew) * rc.c) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      M = mnew;
+      rc.mc = mnew * rc.c;
+    }
+  };
+
+  // ---- main loop --------------------------------------------------------------
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float l = 0.0f;
+  __syncthreads();  // pre-pass reads done before the buffers are refilled
+  load_k(0, 0);
+  load_v(0, 0);
+  if (T > 1) load_k(1, 1);
+  loads_done();
+  store_v(0);
+  __syncthreads();  // also publishes the K-interval tables
+  f32x16 s[2];
+  if (wlast >= 0) qk(0, s, init16);
+  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+  for (int t = 0; t < T; ++t) {
+    if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
+    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
+    if (t < wlast) {
+      if (PV8) {
+        const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+        uint32_t P8[8];
+        weights8(s, P8, l, t, false);
+        const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
+        pv8(t & 1, P8, o);
+        s[0] = sn0;
+        s[1] = sn1;
+      } else {
+        const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+        if (WK == WK_EXACT) online_max(s, o, l);
+        u32x4 P[2];
+        weights16(s[0], 0, P, l, t, false);
+        pv1(t & 1, 0, P, o);
+        const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
+        weights16(s[1], 1, P, l, t, false);
+        pv1(t & 1, 1, P, o);
+        s[0] = sn0;
+        s[1] = sn1;
+      }
+    } else if (t == wlast) {
+      if (PV8) {
+        uint32_t P8[8];
+        weights8(s, P8, l, t, last_masked);
+        pv8(t & 1, P8, o);
+      } else {
+        if (WK == WK_EXACT) {
+          f32x16 sm[2] = {s[0], s[1]};
+          if (last_masked) mask_fill(sm, t, -__builtin_inff());
+          online_max(sm, o, l);
+        }
+        u32x4 P[2];
+        weights16(s[0], 0, P, l, t, last_masked);
+        pv1(t & 1, 0, P, o);
+        weights16(s[1], 1, P, l, t, last_masked);
+        pv1(t & 1, 1, P, o);
+      }
+    }
+    loads_done();
+    if (t + 1 < T) store_v((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  if (wlast < 0) return;
+  const float lt = half_sum(l);
+  if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+    uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+    for (int key = (wlast + 1) * BN + hh; key < N; key += 2) dst[key] = 255u;
+  }
+  if (row >= N) return;
+  __bf16* Og = (__bf16*)a.o + (size_t)(b * a.H + h) * N * D;
+  const float inv = a.vd / lt;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int dcol = db * 32 + 8 * g4 + 4 * hh;
+      const u32x2 v = {pack_bf16(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv),
+                       pack_bf16(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+      *(u32x2*)(Og + (size_t)row * D + dcol) = v;
+    }
+  if (hh == 0) {
+    const size_t ri = (size_t)bh * N + row;
+    if (a.row_max) a.row_max[ri] = M * a.sc;
+    if (a.row_sum) a.row_sum[ri] = PV8 ? 0.5f * lt : lt;  // PoT P carries 2^(1-e)
+    if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
+  }
+#endif
+}
+
+template <int D, int WK>
+hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
+  FwdArgs a = a0;
+  a.n_qtiles = (a.N + BM - 1) / BM;
+  a.total_blocks = a.B * a.H * a.n_qtiles;
+  constexpr bool PV8 = (WK == WK_POT || WK == WK_POT_FLUSH);
+  constexpr int SK = D / 16 + 1, SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);
+  const size_t lds = 2 * (size_t)BN * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
+  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true> : (const void*)fwd_fp8<D, WK, false>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (a.grid_idx)
+    hipLaunchKernelGGL((fwd_fp8<D, WK, true>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+  else
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
+  switch (wk) {
+    case WK_EXACT: return launch_one<D, WK_EXACT>(a, st);
+    case WK_EXACT_ANCH: return launch_one<D, WK_EXACT_ANCH>(a, st);
+    case WK_POT: return launch_one<D, WK_POT>(a, st);
+    case WK_POT_FLUSH: return launch_one<D, WK_POT_FLUSH>(a, st);
+    case WK_KH: return launch_one<D, WK_KH>(a, st);
+    case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
+    case WK_KI: return launch_one<D, WK_KI>(a, st);
+    case WK_KI_FLUSH: return launch_one<D, WK_KI_FLUSH>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fp8(const FwdArgs& a, int d, int wk, hipStream_t st) {
+  if (d == 64) return launch_d<64>(a, wk, st);
+  if (d == 128) return launch_d<128>(a, wk, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qsa

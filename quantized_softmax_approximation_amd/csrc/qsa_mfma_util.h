@@ -1,0 +1,75 @@
+// Device helpers shared by the MFMA attention kernels of libqsa (gfx950).
+#pragma once
+
+#include "qsa_common.h"
+#include "qsa_weights.h"
+
+namespace qsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+
+__device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
+// 32x32x64 8-bit MMA: A in OCP fp8 e4m3, B in e4m3 (fmt_b = 0) or bf8 e5m2 (fmt_b = 1).
+template <int FMT_B>
+__device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, FMT_B, 0, 0, 0, 0);
+}
+
+// Round-to-nearest-even pack of two floats into two bf16 (low = a).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + the two bf16 of p (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_ones(uint32_t p, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+}
+
+// max / min / sum of a value held by lane l and lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fmaxf(bitsf(r[0]), bitsf(r[1]));
+}
+__device__ __forceinline__ float half_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fminf(bitsf(r[0]), bitsf(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
+
+// Key of accumulator register r of lane half hh in a 32x32 S^T block.
+__device__ __forceinline__ int acc_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// Two bf16 weights 2^-e0, 2^-e1 (e clipped to L-1) from t = 2^24 - y (rounded).
+// The low halves of bits(t) are -e as int16; v_pk_mad_u16 turns the pair into
+// the bf16 exponent fields (127 - e) << 7 and v_pk_max_i16 applies the clip.
+__device__ __forceinline__ uint32_t pot_pair(float t0, float t1, uint32_t lo_clip) {
+  const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+  uint32_t w;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(w) : "v"(ne), "v"(0x00800080u), "v"(0x3F803F80u));
+  const s16x2 c = __builtin_elementwise_max(__builtin_bit_cast(s16x2, w), __builtin_bit_cast(s16x2, lo_clip));
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+}  // namespace qsa

@@ -206,3 +206,34 @@ def test_errors_raise_without_launch():
     with pytest.raises(qsa.QSAError) as e:
         qsa.attn_fwd(k, k, k, kind="kint", levels=0)
     assert e.value.status == qsa.ERR_PARAM
+
+
+# ---------------------------------------------------------------- fp8 e4m3 at 8K (per-tensor descales)
+
+@pytest.fixture(scope="module")
+def fp8_8k():
+    wl = qin.WORKLOADS["fp8_8k"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+FP8_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT8, gc.POT4F, gc.KH16W, gc.KH16, gc.KI16W, gc.KH4WF]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("var", FP8_VARS, ids=gc.name)
+def test_fp8_8k_sampled(fp8_8k, var, causal):
+    wl, x, dev_t, f64 = fp8_8k
+    gc.run_parity(wl.replace(causal=causal), var, heads=[(0, 0), (0, 17), (0, 31)],
+                  windows=gc.sample_windows(wl.N, n=3, seed=8), x=x, dev_t=dev_t, f64=f64)
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 333])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ragged(N, d, causal):
+    wl = qin.custom(f"fp8_{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype="fp8", causal=causal, sigma_qk=1.5, seed=3 * N + d)
+    x = qin.make_inputs(wl)
+    dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF):
+        gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
