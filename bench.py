@@ -177,6 +177,9 @@ def main(argv=None):
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--variant-calls", type=int, default=100)
     ap.add_argument("--only-kernel", action="store_true", help="just the timed loop (for profilers)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --only-kernel: also run a plain device copy of this many bytes `steps` times "
+                         "(the known-size reference for HBM traffic counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,7 +212,13 @@ def main(argv=None):
     fn = lambda: call(dev_t, x, var, causal, out)  # noqa: E731
     if args.only_kernel:
         ms, _ = time_loop(fn, args.steps, args.warmup)
-        print(json.dumps({"ms_per_launch": ms}))
+        rec = {"ms_per_launch": ms}
+        if args.copy_bytes:
+            src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            cms, _ = time_loop(lambda: dst.copy_(src), args.steps, 2)
+            rec.update(copy_bytes=src.numel() * 4, copy_ms=cms)
+        print(json.dumps(rec))
         return 0
 
     torch.cuda.synchronize()

@@ -59,12 +59,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr int KT = BN * KR, VT = BN * VR;
   constexpr int KIW = (SK + NW - 1) / NW;
   constexpr int VIW = (SV + NW - 1) / NW;
+  // PoT: K loads run three tiles ahead (three buffers) and V loads two (three buffers), so
+  // that a tile has a whole iteration to land.  The other kinds keep K two tiles ahead and a
+  // register-staged V one tile ahead (two buffers each), which measures faster for them.
+  constexpr int NKB = PV8 ? 3 : 2, NVB = PV8 ? 3 : 2;
+  constexpr int VB0 = NKB * KT;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* const Tb = smem + 2 * KT + 2 * VT;  // K-interval tables
+  unsigned char* const Tb = smem + VB0 + NVB * VT;  // K-interval tables
   lds_u8* const lds = (lds_u8*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // PoT issues its prefetches inside per-wave branches: a wave index the compiler knows to be
+  // uniform keeps those loads' buffer descriptors in SGPRs (the other kinds prefetch outside
+  // any branch and do better, in registers, without it)
+  const int wave = PV8 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int li = lane & 31, hh = lane >> 5;
   int bh, qt;
   map_block(a, bh, qt);
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       for (int m = 0; m < VIW; ++m)
         if (wave + NW * m < SV)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              r, (__attribute__((address_space(3))) void*)(lds + 2 * KT + buf * VT + (wave + NW * m) * 1024), 16,
+              r, (__attribute__((address_space(3))) void*)(lds + VB0 + buf * VT + (wave + NW * m) * 1024), 16,
               vvo[m], 0, 0, 0);
     } else {
 #pragma unroll
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   };
   auto store_v = [&](int buf) {  // bf16-PV kinds: widen the staged quarter row into the bf16 tile
     if (!PV8) {
-      lds_u8* dst = lds + 2 * KT + buf * VT + vrow * VR + vpart * VQ * 2;
+      lds_u8* dst = lds + VB0 + buf * VT + vrow * VR + vpart * VQ * 2;
 #pragma unroll
       for (int m = 0; m < VQL; ++m) {
         u32x4 w0, w1;
@@ -169,6 +178,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
   };
   auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // Wait for this wave's LDS-direct loads except the newest N.  Tile loads are split over the
+  // waves (wave w issues slots w, w+NW, ...), so every wave issues at least SLOTS/NW per tile;
+  // leaving that many in flight is exact for some waves and conservative for the rest.
+  constexpr int NK_MIN = SK / NW, NV_MIN = PV8 ? SV / NW : 0;
+  auto loads_done_but = [&](auto n) {
+    constexpr int N = DUMP ? 0 : decltype(n)::value;  // the index dump's stores also count in vmcnt
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  };
 
   // QK operand reads: lane (li, hh), k-step c: 32 bytes of K row li at 64c + 32hh
   const uint32_t koff = li * KR + hh * 32;
@@ -191,7 +208,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // bf16 PV (exact / K-interval): V^T operand via 16-bit transposing reads of the bf16 tile
   const uint32_t vtr16 = (4 * hh + ((lane & 15) >> 2)) * VR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
-    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr16;
+    const lds_u8* vbase = lds + VB0 + buf * VT + vtr16;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -210,20 +227,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // V[row q][8p .. 8p+7] of the group's 16 columns, row q = key 4hh + q%4 + 8(q/4) (+16 per read).
   const uint32_t vtr8 = (4 * hh + (((lane & 15) >> 1) & 3) + 8 * ((lane & 15) >> 3)) * VR +
                         16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-  auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB]) {
-    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr8;
+  // mid() runs after the V operand reads are issued and before the MMAs
+  auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB], auto&& mid) {
+    const lds_u8* vbase = lds + VB0 + buf * VT + vtr8;
     const i32x8 pb = {(int)P8[0], (int)P8[1], (int)P8[2], (int)P8[3], (int)P8[4], (int)P8[5], (int)P8[6], (int)P8[7]};
+    i32x8 va[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      i32x8 va;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vbase + 16 * k * VR + 32 * db));
-        va[2 * k] = v2[0];
-        va[2 * k + 1] = v2[1];
+        va[db][2 * k] = v2[0];
+        va[db][2 * k + 1] = v2[1];
       }
-      o[db] = mma8<1>(va, pb, o[db]);
-    }
+    mid();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = mma8<1>(va[db], pb, o[db]);
   };
   const int lim = a.causal ? min(row, N - 1) : N - 1;
   auto mask_fill = [&](f32x16 (&s)[2], int kt, float fill) {
@@ -238,18 +257,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   const f32x16 zero16 = {};
   if (ANCH) {
     const bool tmin = a.track_min;
-    load_k(0, 0);
-    if (T > 1) load_k(1, 1);
+    for (int j = 0; j < NKB; ++j)
+      if (j < T) load_k(j, j);
     loads_done();
     __syncthreads();
     f32x16 s[2];
     if (wlast >= 0) qk(0, s, zero16);
     __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+    int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
     for (int t = 0; t < T; ++t) {
-      if (t + 2 < T) load_k(t + 2, t & 1);
+      if (t + NKB < T) load_k(t + NKB, kl);  // buffer of K(t), last read in iteration t-1
       if (t < wlast) {
         f32x16 sn[2];
-        qk((t + 1) & 1, sn, zero16);
+        qk(kn, sn, zero16);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -277,8 +297,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
             for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
         }
       }
-      loads_done();
-      __syncthreads();
+      if (NKB == 3 && t + 3 < T) {
+        loads_done_but(std::integral_constant<int, NK_MIN>());  // K(t+2) has landed, K(t+3) may not
+        lds_barrier();
+      } else {
+        loads_done();
+        __syncthreads();
+      }
+      kl = kn;
+      kn = kn + 1 == NKB ? 0 : kn + 1;
     }
     M = half_max(M);
     MN = half_min(MN);
@@ -439,34 +466,44 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float l = 0.0f;
   __syncthreads();  // pre-pass reads done before the buffers are refilled
-  load_k(0, 0);
   load_v(0, 0);
-  if (T > 1) load_k(1, 1);
+  for (int j = 0; j < NKB; ++j)
+    if (j < T) load_k(j, j);
   loads_done();
   store_v(0);
+  if (PV8 && T > 1) load_v(1, 1);  // PoT: LDS-direct V loads run two tiles ahead too
   __syncthreads();  // also publishes the K-interval tables
   f32x16 s[2];
   if (wlast >= 0) qk(0, s, init16);
   __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+  int kl = 0, kn = 1, vc = 0;  // buffers of K(t), K(t+1), V(t)
   for (int t = 0; t < T; ++t) {
-    if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
-    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
+    // Prefetch K(t+NKB) into the buffer of K(t) and (PoT) V(t+2) into that of V(t-1): both
+    // last read in iteration t-1.  A PoT wave that multiplies P by V this iteration issues
+    // them after its V reads (the compiler makes transposing LDS reads wait for every
+    // LDS-direct load issued before them); other waves and kinds issue them right away.
+    auto prefetch = [&]() {
+      if (t + NKB < T) load_k(t + NKB, kl);
+      if (PV8 && t + 2 < T) load_v(t + 2, vc == 0 ? 2 : vc - 1);
+    };
+    if (!PV8 || t > wlast) prefetch();
+    if (!PV8 && t + 1 < T) load_v(t + 1, (t + 1) & 1);  // register-staged, widened at the end
     if (t < wlast) {
       if (PV8) {
-        const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+        const f32x16 sn0 = qk1(kn, 0, init16);
         uint32_t P8[8];
         weights8(s, P8, l, t, false);
-        const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
-        pv8(t & 1, P8, o);
+        const f32x16 sn1 = qk1(kn, 1, init16);
+        pv8(vc, P8, o, prefetch);
         s[0] = sn0;
         s[1] = sn1;
       } else {
-        const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+        const f32x16 sn0 = qk1(kn, 0, init16);
         if (WK == WK_EXACT) online_max(s, o, l);
         u32x4 P[2];
         weights16(s[0], 0, P, l, t, false);
         pv1(t & 1, 0, P, o);
-        const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
+        const f32x16 sn1 = qk1(kn, 1, init16);
         weights16(s[1], 1, P, l, t, false);
         pv1(t & 1, 1, P, o);
         s[0] = sn0;
@@ -476,7 +513,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       if (PV8) {
         uint32_t P8[8];
         weights8(s, P8, l, t, last_masked);
-        pv8(t & 1, P8, o);
+        pv8(vc, P8, o, prefetch);
       } else {
         if (WK == WK_EXACT) {
           f32x16 sm[2] = {s[0], s[1]};
@@ -490,9 +527,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         pv1(t & 1, 1, P, o);
       }
     }
-    loads_done();
-    if (t + 1 < T) store_v((t + 1) & 1);
-    __syncthreads();
+    if (PV8) {
+      // K(t+2) and V(t+1), loaded last iteration, have landed; this iteration's may not have
+      if (t + 3 < T)
+        loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
+      else if (t + 2 < T)
+        loads_done_but(std::integral_constant<int, NV_MIN>());
+      else
+        loads_done();
+      lds_barrier();
+    } else {
+      loads_done();
+      if (t + 1 < T) store_v((t + 1) & 1);  // register-staged V, widened to bf16
+      __syncthreads();
+    }
+    kl = kn;
+    kn = kn + 1 == NKB ? 0 : kn + 1;
+    vc = vc + 1 == NVB ? 0 : vc + 1;
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -530,7 +581,8 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   a.total_blocks = a.B * a.H * a.n_qtiles;
   constexpr bool PV8 = (WK == WK_POT || WK == WK_POT_FLUSH);
   constexpr int SK = D / 16 + 1, SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);
-  const size_t lds = 2 * (size_t)BN * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
+  constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
+  const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
   const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true> : (const void*)fwd_fp8<D, WK, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -1,6 +1,8 @@
 // Device helpers shared by the MFMA attention kernels of libqsa (gfx950).
 #pragma once
 
+#include <type_traits>
+
 #include "qsa_common.h"
 #include "qsa_weights.h"
 
@@ -19,6 +21,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS operations but not for
+// its outstanding global loads.  (__syncthreads() also drains every global load, which would
+// serialise LDS-direct prefetches issued further ahead; those are waited for with explicit
+// vmcnt waits before this barrier.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
