@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -51,11 +52,16 @@ def mfma_flops_per_pair(kind, d):
 
 
 def src_hash():
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a comment-only edit keeps the recorded counters valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_softmax_approximation_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

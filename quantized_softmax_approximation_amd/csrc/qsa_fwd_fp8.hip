@@ -3,10 +3,11 @@
 //
 // Same structure as the bf16 kernel (one workgroup = 4 waves = 128 query rows;
 // S^T = K Q^T so a lane owns a query row; true-row-max pre-pass; main-loop
-// accumulators start at -M; double-buffered LDS tiles with one barrier per
+// accumulators start at -M; LDS tiles filled ahead of use with one barrier per
 // tile; masking only on a wave's last tile), with the score product on the
 // 8-bit matrix cores: v_mfma_f32_32x32x64_f8f6f4, 64 key-or-feature columns
-// per instruction.
+// per instruction.  PoT keeps three K and three V tile buffers (K three tiles
+// ahead, V two); the other kinds two of each.
 //
 // The PV product depends on whether the weights fit an 8-bit float exactly:
 //   * Rowmax-PoT: the weights 2^-e ("Approximating Softmax in Pretrained
