@@ -232,7 +232,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   f32x16 init16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
-  const uint32_t pot_clip = 0x00010001u * (uint32_t)((128 - a.levels) * 128);  // (127 - (L-1)) << 7, twice
+  const int32_t pot_lo = 0x4B800000 - (a.levels - 1);  // bits of 2^24 - (L-1): the clip e <= L-1
   const int L = a.levels;
   const float Kf = (float)a.levels;
 
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
           } else if (POT && !FLUSH) {
             // t = 2^24 + (acc - M) c = 2^24 - y, rounded to an integer by the FMA itself
             const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
-            pk = pot_pair(t0, t1, pot_clip);
+            pk = pot_pair(t0, t1, pot_lo);
             if (DUMP) {
               i0 = 127u - ((pk >> 7) & 0x1FFu);
               i1 = 127u - ((pk >> 23) & 0x1FFu);

@@ -11,11 +11,15 @@
 //
 // The PV product depends on whether the weights fit an 8-bit float exactly:
 //   * Rowmax-PoT: the weights 2^-e ("Approximating Softmax in Pretrained
-//     LLMs", abstract: power-of-two weights anchored at each row maximum) are
-//     exact in bf8 e5m2 as 2^(1-e), e <= 15, so P^T is built directly as bf8
-//     bytes from the exponent and PV runs on the 8-bit matrix cores with V in
-//     e4m3 (operand formats e4m3 x bf8).  The V^T operand comes from 8-bit
-//     transposing LDS reads (ds_read_b64_tr_b8).
+//     LLMs", abstract: power-of-two weights anchored at each row maximum),
+//     scaled by the constant 2^(L-15), are exact in bf8 e5m2 for e <= L-1 <= 15
+//     (and e = L, the flushed level, is exactly 0), so P^T is built directly as
+//     bf8 bytes from the exponent and PV runs on the 8-bit matrix cores with V
+//     in e4m3 (operand formats e4m3 x bf8).  The V^T operand comes from 8-bit
+//     transposing LDS reads (ds_read_b64_tr_b8).  The row sum of the same bf8
+//     weights is one more 8-bit MMA per tile (16x16x128 against a constant 0/1
+//     selector), which keeps it off the VALU: on gfx950 VALU work of one wave
+//     slows the matrix-core work of the other waves on its SIMD.
 //   * exact and K-interval weights are not representable in 8 bits without
 //     rounding errors of a few percent per row (e4m3 keeps 3 mantissa bits),
 //     so their PV runs in bf16: V tiles are widened e4m3 -> bf16 (exactly)
@@ -32,18 +36,16 @@ constexpr int BN = 64;   // keys per tile
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
 
-// Two PoT weights from t = 2^24 - y (rounded): the clipped exponent pair
-// u = (-e0, -e1) as int16 gives both the bf8 bytes of 2^(1-e) (low byte of each
-// 16-bit half) and the bf16 patterns of the same 2^(1-e) for the row sum.
-__device__ __forceinline__ void pot8_pair(float t0, float t1, uint32_t clip, uint32_t& b8, uint32_t& b16) {
-  const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
-  const s16x2 u = __builtin_elementwise_max(__builtin_bit_cast(s16x2, ne), __builtin_bit_cast(s16x2, clip));
-  const uint32_t uu = __builtin_bit_cast(uint32_t, u);
-  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(b8) : "v"(uu), "v"(0x00040004u), "v"(0x00400040u));   // (16 - e) << 2
-  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(b16) : "v"(uu), "v"(0x00800080u), "v"(0x40004000u));  // (128 - e) << 7
+// v_pk_mad_u16: a * b + c in each 16-bit half
+__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
 }
 
-template <int D, int WK, bool DUMP>
+// WIDE: the score range of a row may exceed 2^15 log2 units, so the exponent is clamped in
+// 32 bits before its low 16 bits are used (the launcher proves when it cannot; PoT only).
+template <int D, int WK, bool DUMP, bool WIDE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
@@ -118,14 +120,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   auto tile_rsrc = [&](const uint8_t* base, int kt) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D, 0x00020000);
   };
-  auto load_k = [&](int kt, int buf) {
+  auto load_k_at = [&](int kt, int off) {  // K tile kt into the LDS bytes at off
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kg, kt);
 #pragma unroll
     for (int m = 0; m < KIW; ++m)
       if (wave + NW * m < SK)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
+            r, (__attribute__((address_space(3))) void*)(lds + off + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
   };
+  auto load_k = [&](int kt, int buf) { load_k_at(kt, buf * KT); };
   uint32_t vvo[PV8 ? VIW : 1];
   if (PV8) {
 #pragma unroll
@@ -222,12 +225,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         o[db] = mma(va, P[kc], o[db]);
       }
   };
-  // fp8 PV (PoT): byte e of the P^T operand is key 16(e/8) + 8((e/4)%2) + 4hh + e%4 of the tile
-  // (accumulator register e%16 of block e/16); 8-bit transposing reads put V[that key][dcol]
-  // in byte e of lane (dcol, hh): in each 16-lane group, lane 2q + p points at
-  // V[row q][8p .. 8p+7] of the group's 16 columns, row q = key 4hh + q%4 + 8(q/4) (+16 per read).
-  const uint32_t vtr8 = (4 * hh + (((lane & 15) >> 1) & 3) + 8 * ((lane & 15) >> 3)) * VR +
+  // fp8 PV (PoT): byte e of the P^T operand is key 16(e/8) + 8((e/4)%2) + 4hh + sg(e%4) of the
+  // tile, sg = (0, 2, 1, 3) (the byte order in which the weights are packed, see weights8);
+  // 8-bit transposing reads put V[that key][dcol] in byte e of lane (dcol, hh): in each
+  // 16-lane group, lane 2q + p points at V[row q][8p .. 8p+7] of the group's 16 columns,
+  // row q = key 4hh + sg(q%4) + 8(q/4) (+16 per read).
+  const int vq = ((lane & 15) >> 1) & 3;
+  const uint32_t vtr8 = (4 * hh + (((vq & 1) << 1) | (vq >> 1)) + 8 * ((lane & 15) >> 3)) * VR +
                         16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  // row-sum MMA selector (16x16x128, A = 16 x 128 e4m3): lane l holds row l % 16 and k-group
+  // l / 16; rows 0-7 take k-groups 0 and 2, rows 8-15 k-groups 1 and 3, as 1.0 (0x38)
+  const int sel = (((lane & 15) < 8) == (((lane >> 4) & 1) == 0)) ? 0x38383838 : 0;
+  const i32x8 rs_sel = {sel, sel, sel, sel, sel, sel, sel, sel};
+  f32x4 rs = {0.0f, 0.0f, 0.0f, 0.0f};  // PoT row sums (see the epilogue for the layout)
   // mid() runs after the V operand reads are issued and before the MMAs
   auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB], auto&& mid) {
     const lds_u8* vbase = lds + VB0 + buf * VT + vtr8;
@@ -244,6 +254,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     mid();
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = mma8<1>(va[db], pb, o[db]);
+    rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rs_sel, pb, rs, 0, 1, 0, 0, 0, 0);
   };
   const int lim = a.causal ? min(row, N - 1) : N - 1;
   auto mask_fill = [&](f32x16 (&s)[2], int kt, float fill) {
@@ -316,8 +327,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   f32x16 init16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
-  const uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(1 - a.levels);  // -(L-1), twice
   const int L = a.levels;
+  // PoT: e is clamped to ec = L-1 (or L with flush, whose level weighs 0); the weight
+  // 2^(L-15-e) is the bf8 byte (L - e) << 2
+  const int ec = FLUSH ? L : L - 1;
+  const uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(-ec);  // -ec, twice (int16)
+  const int32_t pot_lo = 0x4B800000 - ec;                               // bits of 2^24 - ec
+  const uint32_t pot_add = 0x00010001u * (uint32_t)(4 * L * 257);     // 4L in both bytes of a half
   const float Kf = (float)a.levels;
 
   // bf16 weights of 32-key block kb (exact / K-interval), as in the bf16 kernel
@@ -389,58 +405,45 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       }
   };
 
-  // PoT weights of a whole 64-key tile as bf8 bytes (P8) + row sum of the same 2^(1-e)
-  auto weights8 = [&](const f32x16 (&s)[2], uint32_t (&P8)[8], float& l, int kt, bool masked) {
+  // PoT weights of a whole 64-key tile as bf8 bytes (P8); their row sum goes to rs by an MMA.
+  // t = 2^24 - y rounded to an integer (y = (m - s) log2 e >= 0, the FMA rounds to nearest
+  // even): the low 16 bits of its pattern are -e.  For four elements r0..r0+3 the clamped
+  // pairs (-e0, -e1) and (-e2, -e3) become the bytes 4(L - e) in the order r0, r0+2, r0+1,
+  // r0+3 by two v_pk_mad_u16: 4(-e) + 4L*257 gives byte 0 and a carry-free 4L in byte 1 of
+  // each half, then 1024(-e') adds the second pair's bytes in byte 1.
+  auto weights8 = [&](const f32x16 (&s)[2], uint32_t (&P8)[8], int kt, bool masked) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r0 = 4 * (w & 3);
-      uint32_t b8[2];
+      uint32_t u[2];
 #pragma unroll
       for (int hp = 0; hp < 2; ++hp) {
         const int r = r0 + 2 * hp;
-        const float t0 = fmaf(s[kb][r], rc.c, 16777216.0f), t1 = fmaf(s[kb][r + 1], rc.c, 16777216.0f);
-        uint32_t bb, b16;
-        uint32_t i0 = 0, i1 = 0;
-        if (!FLUSH) {
-          pot8_pair(t0, t1, pot_clip, bb, b16);
-          if (DUMP) {
-            const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
-            const s16x2 u = __builtin_elementwise_max(__builtin_bit_cast(s16x2, ne), __builtin_bit_cast(s16x2, pot_clip));
-            i0 = (uint32_t)(-(int)u[0]);
-            i1 = (uint32_t)(-(int)u[1]);
-          }
-        } else {  // e >= L -> 0
-          const int32_t lo = 0x4B800000 - (L - 1);
-          const int32_t c0 = (int32_t)fbits(t0), c1 = (int32_t)fbits(t1);
-          const uint32_t e0 = (uint32_t)(0x4B800000 - c0), e1 = (uint32_t)(0x4B800000 - c1);
-          const uint32_t k0 = c0 < lo ? 0u : 0xFFFFu, k1 = c1 < lo ? 0u : 0xFFFFu;
-          const uint32_t e0c = c0 < lo ? 0u : e0, e1c = c1 < lo ? 0u : e1;
-          bb = (((16u - e0c) << 2) & k0) | ((((16u - e1c) << 2) & k1) << 16);
-          b16 = (((128u - e0c) << 7) & k0) | ((((128u - e1c) << 7) & k1) << 16);
-          if (DUMP) {
-            i0 = c0 < lo ? 254u : e0;
-            i1 = c1 < lo ? 254u : e1;
-          }
+        uint32_t t0 = fbits(fmaf(s[kb][r], rc.c, 16777216.0f)), t1 = fbits(fmaf(s[kb][r + 1], rc.c, 16777216.0f));
+        if (WIDE || DUMP) {  // clamp in 32 bits: exact for any y
+          t0 = (uint32_t)max((int32_t)t0, pot_lo);
+          t1 = (uint32_t)max((int32_t)t1, pot_lo);
         }
-        const int key0 = kt * BN + kb * 32 + acc_key(r, hh);
-        if (masked) {
-          const uint32_t m = (key0 <= lim ? 0x0000FFFFu : 0u) | (key0 + 1 <= lim ? 0xFFFF0000u : 0u);
-          bb &= m;
-          b16 &= m;
-          if (DUMP) {
-            i0 = key0 <= lim ? i0 : 255u;
-            i1 = key0 + 1 <= lim ? i1 : 255u;
-          }
-        }
+        u[hp] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+        if (!(WIDE || DUMP))  // y < 2^15: the 16-bit exponent does not wrap
+          u[hp] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, u[hp]),
+                                                                         __builtin_bit_cast(s16x2, pot_clip)));
         if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
           uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
-          if (key0 < N) dst[key0] = (uint8_t)i0;
-          if (key0 + 1 < N) dst[key0 + 1] = (uint8_t)i1;
+          const int key0 = kt * BN + kb * 32 + acc_key(r, hh);
+          const s16x2 ue = __builtin_bit_cast(s16x2, u[hp]);
+          const int e0 = -(int)ue[0], e1 = -(int)ue[1];
+          if (key0 < N) dst[key0] = key0 > lim ? 255u : (FLUSH && e0 == L) ? 254u : (uint8_t)e0;
+          if (key0 + 1 < N) dst[key0 + 1] = key0 + 1 > lim ? 255u : (FLUSH && e1 == L) ? 254u : (uint8_t)e1;
         }
-        b8[hp] = bb;
-        l = dot2_ones(b16, l);
       }
-      P8[w] = __builtin_amdgcn_perm(b8[1], b8[0], 0x06040200u);  // low bytes of the four halves
+      uint32_t p = pk_mad_u16(u[1], 0x04000400u, pk_mad_u16(u[0], 0x00040004u, pot_add));
+      if (masked) {  // bytes: r0, r0+2, r0+1, r0+3
+        const int key0 = kt * BN + kb * 32 + acc_key(r0, hh);
+        p &= (key0 <= lim ? 0x000000FFu : 0u) | (key0 + 2 <= lim ? 0x0000FF00u : 0u) |
+             (key0 + 1 <= lim ? 0x00FF0000u : 0u) | (key0 + 3 <= lim ? 0xFF000000u : 0u);
+      }
+      P8[w] = p;
     }
   };
 
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       if (PV8) {
         const f32x16 sn0 = qk1(kn, 0, init16);
         uint32_t P8[8];
-        weights8(s, P8, l, t, false);
+        weights8(s, P8, t, false);
         const f32x16 sn1 = qk1(kn, 1, init16);
         pv8(vc, P8, o, prefetch);
         s[0] = sn0;
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     } else if (t == wlast) {
       if (PV8) {
         uint32_t P8[8];
-        weights8(s, P8, l, t, last_masked);
+        weights8(s, P8, t, last_masked);
         pv8(vc, P8, o, prefetch);
       } else {
         if (WK == WK_EXACT) {
@@ -549,7 +552,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 
   // ---- epilogue -----------------------------------------------------------
   if (wlast < 0) return;
-  const float lt = half_sum(l);
+  // PoT: the row-sum MMA leaves the sum of query n (+16) in lanes n, n+16 (n+32, n+48), register 0
+  const float lt = PV8 ? bitsf(__builtin_amdgcn_ds_bpermute(4 * (li < 16 ? li : li + 16), (int)fbits(rs[0])))
+                       : half_sum(l);
   if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
     uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
     for (int key = (wlast + 1) * BN + hh; key < N; key += 2) dst[key] = 255u;
@@ -569,7 +574,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   if (hh == 0) {
     const size_t ri = (size_t)bh * N + row;
     if (a.row_max) a.row_max[ri] = M * a.sc;
-    if (a.row_sum) a.row_sum[ri] = PV8 ? 0.5f * lt : lt;  // PoT P carries 2^(1-e)
+    if (a.row_sum) a.row_sum[ri] = PV8 ? __builtin_ldexpf(lt, 15 - L) : lt;  // PoT P carries 2^(L-15)
     if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
   }
 #endif
@@ -584,15 +589,21 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   constexpr int SK = D / 16 + 1, SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
   const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
-  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true> : (const void*)fwd_fp8<D, WK, false>;
+  // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
+  // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does
+  const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
+  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false>
+                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8> : (const void*)fwd_fp8<D, WK, false, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, true>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+  else if (wide)
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 

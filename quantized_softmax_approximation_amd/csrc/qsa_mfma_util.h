@@ -11,6 +11,7 @@ namespace qsa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -70,14 +71,15 @@ __device__ __forceinline__ float half_sum(float x) {
 __device__ __forceinline__ int acc_key(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
 // Two bf16 weights 2^-e0, 2^-e1 (e clipped to L-1) from t = 2^24 - y (rounded).
-// The low halves of bits(t) are -e as int16; v_pk_mad_u16 turns the pair into
-// the bf16 exponent fields (127 - e) << 7 and v_pk_max_i16 applies the clip.
-__device__ __forceinline__ uint32_t pot_pair(float t0, float t1, uint32_t lo_clip) {
-  const uint32_t ne = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+// bits(t) = 0x4B800000 - e; the clip is an integer max in 32 bits (so any y is
+// clipped correctly), after which the low halves are -e as int16 and one
+// v_pk_mad_u16 turns the pair into the bf16 exponent fields (127 - e) << 7.
+__device__ __forceinline__ uint32_t pot_pair(float t0, float t1, int32_t lo) {
+  const uint32_t b0 = (uint32_t)max((int32_t)fbits(t0), lo), b1 = (uint32_t)max((int32_t)fbits(t1), lo);
+  const uint32_t ne = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
   uint32_t w;
   asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(w) : "v"(ne), "v"(0x00800080u), "v"(0x3F803F80u));
-  const s16x2 c = __builtin_elementwise_max(__builtin_bit_cast(s16x2, w), __builtin_bit_cast(s16x2, lo_clip));
-  return __builtin_bit_cast(uint32_t, c);
+  return w;
 }
 
 }  // namespace qsa

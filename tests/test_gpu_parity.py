@@ -121,6 +121,17 @@ def test_large_levels_and_windows():
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_very_wide_score_range(dtype):
+    # logit std ~6400: score gaps far beyond 2^15 log2 units, where a 16-bit exponent field
+    # would wrap; every weight past the clip must still be the last level (or 0 with flush)
+    wl = qin.custom(f"wide_{dtype}", B=1, H=2, N=200, d=128, dtype=dtype, causal=True, sigma_qk=80.0, seed=11)
+    x = qin.make_inputs(wl)
+    dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+    for var in (gc.POT8, gc.POT16, gc.POT4F, gc.EXACT_ANCH, gc.KH4):
+        gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64)
+
+
 def test_degenerate_rows_all_scores_equal():
     # q = 0: every score is 0; min-max grids have zero width, all weights 1
     wl = qin.custom("flat", B=1, H=2, N=130, d=64, dtype="bf16", causal=True, seed=4)
