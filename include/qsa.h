@@ -35,7 +35,10 @@
  *             qsa_fwd_ex_opts); O is bfloat16.
  *   Pointers  Q, K, V, O and every optional output are DEVICE pointers owned
  *             by the caller.  The library allocates nothing, keeps no state
- *             between calls and needs no workspace.
+ *             between calls and needs no workspace.  O must not overlap Q, K
+ *             or V: for fp8 inputs and the anchored kinds the call runs two
+ *             kernels on `stream`, and the first parks each row's score
+ *             extrema in that row of O for the second.
  *   Streams   `stream` is a hipStream_t passed as void* (NULL: the null
  *             stream).  A call only enqueues work and returns; the caller
  *             synchronises.  Calls are reentrant and thread-safe.

@@ -36,6 +36,13 @@ constexpr int BN = 64;   // keys per tile
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
 
+// Slot of 16-byte chunk c of fp8 V row r is c ^ vswz(r) (row bits 1 and 3 for d = 128, bit 3
+// for d = 64 pick the chunk pair): conflict-free 8-bit transposing reads of the PoT V tile.
+template <int D>
+__device__ __forceinline__ int vswz_of(int r) {
+  return D == 128 ? 2 * (((r >> 1) & 1) | ((r >> 2) & 2)) : 2 * ((r >> 3) & 1);
+}
+
 // v_pk_mad_u16: a * b + c in each 16-bit half
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
@@ -45,8 +52,14 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 
 // WIDE: the score range of a row may exceed 2^15 log2 units, so the exponent is clamped in
 // 32 bits before its low 16 bits are used (the launcher proves when it cannot; PoT only).
-template <int D, int WK, bool DUMP, bool WIDE>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
+// PH: 0 = the whole forward in one launch (the online exact kind, which has no pre-pass);
+// 1 = the row-extrema pre-pass alone: it parks each row's extrema in the row's first 8 bytes
+// of O and, with few registers live, runs at 3 waves per SIMD instead of 2; 2 = everything
+// after the pre-pass, which reads the extrema back before it writes O.  Splitting the
+// anchored kinds into launches 1 and 2 measured 2 % faster for exact-anchored and K-interval
+// and the same for PoT.
+template <int D, int WK, bool DUMP, bool WIDE, int PH>
+__global__ __launch_bounds__(NW * 64, PH == 1 ? 3 : 2) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
@@ -57,8 +70,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
   constexpr bool PV8 = POT;
   constexpr int SK = D / 16 + 1;                      // 16-byte slots per K row (odd)
-  constexpr int SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);  // fp8 V rows, or bf16 rows (stride 64 mod 256)
+  constexpr int SV = PV8 ? D / 16 : (D / 8 + 4);  // fp8 V rows (swizzled, unpadded), or bf16 rows (stride 64 mod 256)
   constexpr int KR = SK * 16, VR = SV * 16;
+  auto vswz = [](int r) { return vswz_of<D>(r); };
   constexpr int KT = BN * KR, VT = BN * VR;
   constexpr int KIW = (SK + NW - 1) / NW;
   constexpr int VIW = (SV + NW - 1) / NW;
@@ -133,8 +147,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   if (PV8) {
 #pragma unroll
     for (int m = 0; m < VIW; ++m) {
-      const int sl = (wave + NW * m) * 64 + lane, j = sl / SV, c = sl % SV;
-      vvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+      const int sl = (wave + NW * m) * 64 + lane, j = sl / SV;
+      vvo[m] = (uint32_t)(j * D + ((sl % SV) ^ vswz(j)) * 16);  // slot (j, c') holds chunk c' ^ vswz(j)
     }
   }
   // bf16-PV kinds: each thread widens a quarter row of V (D/4 fp8 -> bf16) into LDS
@@ -183,9 +197,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   };
   auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // Wait for this wave's LDS-direct loads except the newest N.  Tile loads are split over the
-  // waves (wave w issues slots w, w+NW, ...), so every wave issues at least SLOTS/NW per tile;
-  // leaving that many in flight is exact for some waves and conservative for the rest.
+  // waves (wave w issues slots w, w+NW, ...): SLOTS/NW of them, plus one when w < SLOTS % NW.
   constexpr int NK_MIN = SK / NW, NV_MIN = PV8 ? SV / NW : 0;
+  static_assert(!PV8 || SV % NW == 0, "PoT V tiles split evenly over the waves");
   auto loads_done_but = [&](auto n) {
     constexpr int N = DUMP ? 0 : decltype(n)::value;  // the index dump's stores also count in vmcnt
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -229,10 +243,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // tile, sg = (0, 2, 1, 3) (the byte order in which the weights are packed, see weights8);
   // 8-bit transposing reads put V[that key][dcol] in byte e of lane (dcol, hh): in each
   // 16-lane group, lane 2q + p points at V[row q][8p .. 8p+7] of the group's 16 columns,
-  // row q = key 4hh + sg(q%4) + 8(q/4) (+16 per read).
-  const int vq = ((lane & 15) >> 1) & 3;
-  const uint32_t vtr8 = (4 * hh + (((vq & 1) << 1) | (vq >> 1)) + 8 * ((lane & 15) >> 3)) * VR +
-                        16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  // row q = key 4hh + sg(q%4) + 8(q/4) (+16 per read).  16-byte chunk c of V row r sits in
+  // slot c ^ vswz(r) of the row, which spreads the 32 lanes of each half-wave read over all 64
+  // LDS banks (vswz depends on row bits 1-3 only, so the +16-row reads keep it).
+  int vtr8[DB];
+  {
+    const int vq = ((lane & 15) >> 1) & 3;
+    const int vr = 4 * hh + (((vq & 1) << 1) | (vq >> 1)) + 8 * ((lane & 15) >> 3);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vtr8[db] = vr * VR + 16 * ((2 * db + ((lane >> 4) & 1)) ^ vswz(vr)) + 8 * (lane & 1);
+  }
   // row-sum MMA selector (16x16x128, A = 16 x 128 e4m3): lane l holds row l % 16 and k-group
   // l / 16; rows 0-7 take k-groups 0 and 2, rows 8-15 k-groups 1 and 3, as 1.0 (0x38)
   const int sel = (((lane & 15) < 8) == (((lane >> 4) & 1) == 0)) ? 0x38383838 : 0;
@@ -240,14 +261,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   f32x4 rs = {0.0f, 0.0f, 0.0f, 0.0f};  // PoT row sums (see the epilogue for the layout)
   // mid() runs after the V operand reads are issued and before the MMAs
   auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB], auto&& mid) {
-    const lds_u8* vbase = lds + VB0 + buf * VT + vtr8;
+    const lds_u8* vbase = lds + VB0 + buf * VT;
     const i32x8 pb = {(int)P8[0], (int)P8[1], (int)P8[2], (int)P8[3], (int)P8[4], (int)P8[5], (int)P8[6], (int)P8[7]};
     i32x8 va[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vbase + 16 * k * VR + 32 * db));
+        const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vbase + vtr8[db] + 16 * k * VR));
         va[db][2 * k] = v2[0];
         va[db][2 * k + 1] = v2[1];
       }
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // ---- pre-pass: true row extrema ------------------------------------------
   float M = -__builtin_inff(), MN = __builtin_inff();
   const f32x16 zero16 = {};
-  if (ANCH) {
+  if (ANCH && PH != 2) {
     const bool tmin = a.track_min;
     for (int j = 0; j < NKB; ++j)
       if (j < T) load_k(j, j);
@@ -321,6 +342,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
     M = half_max(M);
     MN = half_min(MN);
+  }
+  uint32_t* const park = (uint32_t*)((__bf16*)a.o + ((size_t)(b * a.H + h) * N + row) * D);
+  if (PH == 1) {
+    if (hh == 0 && row < N) {
+      park[0] = fbits(M);
+      park[1] = fbits(MN);
+    }
+    return;
+  }
+  if (PH == 2) {
+    M = row < N ? bitsf(park[0]) : 0.0f;
+    MN = row < N ? bitsf(park[1]) : 0.0f;
   }
 
   RowC rc = make_row<WK, SH>(a, M, MN, wave * 32 + li, Tb, hh, 2);
@@ -533,9 +566,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
     if (PV8) {
       // K(t+2) and V(t+1), loaded last iteration, have landed; this iteration's may not have
-      if (t + 3 < T)
-        loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
-      else if (t + 2 < T)
+      if (t + 3 < T) {
+        if (wave < SK % NW)
+          loads_done_but(std::integral_constant<int, NK_MIN + 1 + NV_MIN>());
+        else
+          loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
+      } else if (t + 2 < T)
         loads_done_but(std::integral_constant<int, NV_MIN>());
       else
         loads_done();
@@ -586,24 +622,32 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.total_blocks = a.B * a.H * a.n_qtiles;
   constexpr bool PV8 = (WK == WK_POT || WK == WK_POT_FLUSH);
-  constexpr int SK = D / 16 + 1, SV = PV8 ? (D / 16 + 1) : (D / 8 + 4);
+  constexpr bool ANCH = WK != WK_EXACT;
+  constexpr int SK = D / 16 + 1, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
   const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
+  constexpr int PHM = ANCH ? 2 : 0;  // phase of the main launch
   // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
   // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does
   const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
-  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false>
-                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8> : (const void*)fwd_fp8<D, WK, false, false>;
+  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false, PHM>
+                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8, PHM> : (const void*)fwd_fp8<D, WK, false, false, PHM>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  if constexpr (ANCH) {  // the pre-pass needs only the K buffers
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false, 1>), dim3(a.total_blocks), dim3(NW * 64),
+                       (size_t)BN * NB * SK * 16, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else if (wide)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
