@@ -54,12 +54,12 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 // 32 bits before its low 16 bits are used (the launcher proves when it cannot; PoT only).
 // PH: 0 = the whole forward in one launch (the online exact kind, which has no pre-pass);
 // 1 = the row-extrema pre-pass alone: it parks each row's extrema in the row's first 8 bytes
-// of O and, with few registers live, runs at 3 waves per SIMD instead of 2; 2 = everything
+// of O and, with few registers live, runs at 4 waves per SIMD instead of 2; 2 = everything
 // after the pre-pass, which reads the extrema back before it writes O.  Splitting the
 // anchored kinds into launches 1 and 2 measured 2 % faster for exact-anchored and K-interval
 // and the same for PoT.
 template <int D, int WK, bool DUMP, bool WIDE, int PH>
-__global__ __launch_bounds__(NW * 64, PH == 1 ? 3 : 2) void fwd_fp8(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, PH == 1 ? 4 : 2) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
@@ -87,10 +87,10 @@ __global__ __launch_bounds__(NW * 64, PH == 1 ? 3 : 2) void fwd_fp8(FwdArgs a) {
   lds_u8* const lds = (lds_u8*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // PoT issues its prefetches inside per-wave branches: a wave index the compiler knows to be
-  // uniform keeps those loads' buffer descriptors in SGPRs (the other kinds prefetch outside
-  // any branch and do better, in registers, without it)
-  const int wave = PV8 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  // PoT's main loop issues its prefetches inside per-wave branches: a wave index the compiler
+  // knows to be uniform keeps those loads' buffer descriptors in SGPRs (the other kinds, and
+  // the pre-pass, prefetch outside any branch and need fewer registers without it)
+  const int wave = (PV8 && PH != 1) ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int li = lane & 31, hh = lane >> 5;
   int bh, qt;
   map_block(a, bh, qt);
