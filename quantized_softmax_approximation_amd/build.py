@@ -26,6 +26,11 @@ ARCH = "gfx950"
 # Packed-FP32 VALU instructions are kept out of the device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+# Per-file code-generation flags.  The MFMA kernels schedule for instruction-level parallelism
+# rather than occupancy (they run at 2 waves per SIMD either way): measured 1-3.5 % faster for
+# every kind at 8K, fp8 and bf16.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+FILE_FLAGS = {"qsa_fwd_fp8.hip": _ILP, "qsa_fwd_bf16.hip": _ILP}
 
 
 def hipcc() -> str:
@@ -41,7 +46,7 @@ def sources():
 
 def _compile(src: str, extra, objdir: str = OBJDIR) -> str:
     obj = os.path.join(objdir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
