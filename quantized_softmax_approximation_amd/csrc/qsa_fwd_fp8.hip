@@ -52,14 +52,10 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 
 // WIDE: the score range of a row may exceed 2^15 log2 units, so the exponent is clamped in
 // 32 bits before its low 16 bits are used (the launcher proves when it cannot; PoT only).
-// PH: 0 = the whole forward in one launch (the online exact kind, which has no pre-pass);
-// 1 = the row-extrema pre-pass alone: it parks each row's extrema in the row's first 8 bytes
-// of O and, with few registers live, runs at 4 waves per SIMD instead of 2; 2 = everything
-// after the pre-pass, which reads the extrema back before it writes O.  Splitting the
-// anchored kinds into launches 1 and 2 measured 2 % faster for exact-anchored and K-interval
-// and the same for PoT.
-template <int D, int WK, bool DUMP, bool WIDE, int PH>
-__global__ __launch_bounds__(NW * 64, PH == 1 ? 4 : 2) void fwd_fp8(FwdArgs a) {
+// Anchored kinds (all but the online exact control) run after rowext_fp8, which leaves each
+// row's score extrema parked in O; the kernel reads them back before it writes O.
+template <int D, int WK, bool DUMP, bool WIDE>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
@@ -88,9 +84,9 @@ __global__ __launch_bounds__(NW * 64, PH == 1 ? 4 : 2) void fwd_fp8(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   // PoT's main loop issues its prefetches inside per-wave branches: a wave index the compiler
-  // knows to be uniform keeps those loads' buffer descriptors in SGPRs (the other kinds, and
-  // the pre-pass, prefetch outside any branch and need fewer registers without it)
-  const int wave = (PV8 && PH != 1) ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  // knows to be uniform keeps those loads' buffer descriptors in SGPRs (the other kinds
+  // prefetch outside any branch and need fewer registers without it)
+  const int wave = PV8 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int li = lane & 31, hh = lane >> 5;
   int bh, qt;
   map_block(a, bh, qt);
@@ -285,73 +281,12 @@ __global__ __launch_bounds__(NW * 64, PH == 1 ? 4 : 2) void fwd_fp8(FwdArgs a) {
       for (int r = 0; r < 16; ++r) s[kb][r] = (kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : fill;
   };
 
-  // ---- pre-pass: true row extrema ------------------------------------------
+  // ---- row extrema of the anchored kinds ------------------------------------
+  // rowext_fp8 parked them as raw accumulator values, 8 bytes per row packed at the start of
+  // the wave's own 32 rows of O (a contiguous 256-byte run), which this wave later overwrites
   float M = -__builtin_inff(), MN = __builtin_inff();
-  const f32x16 zero16 = {};
-  if (ANCH && PH != 2) {
-    const bool tmin = a.track_min;
-    for (int j = 0; j < NKB; ++j)
-      if (j < T) load_k(j, j);
-    loads_done();
-    __syncthreads();
-    f32x16 s[2];
-    if (wlast >= 0) qk(0, s, zero16);
-    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-    int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
-    for (int t = 0; t < T; ++t) {
-      if (t + NKB < T) load_k(t + NKB, kl);  // buffer of K(t), last read in iteration t-1
-      if (t < wlast) {
-        f32x16 sn[2];
-        qk(kn, sn, zero16);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
-        if (tmin) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
-        }
-        s[0] = sn[0];
-        s[1] = sn[1];
-      } else if (t == wlast) {
-        f32x16 sm[2] = {s[0], s[1]};
-        if (last_masked) mask_fill(sm, t, -__builtin_inff());
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) M = fmaxf(M, sm[kb][r]);
-        if (tmin) {
-          if (last_masked) mask_fill(s, t, __builtin_inff());
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
-        }
-      }
-      if (NKB == 3 && t + 3 < T) {
-        loads_done_but(std::integral_constant<int, NK_MIN>());  // K(t+2) has landed, K(t+3) may not
-        lds_barrier();
-      } else {
-        loads_done();
-        __syncthreads();
-      }
-      kl = kn;
-      kn = kn + 1 == NKB ? 0 : kn + 1;
-    }
-    M = half_max(M);
-    MN = half_min(MN);
-  }
-  uint32_t* const park = (uint32_t*)((__bf16*)a.o + ((size_t)(b * a.H + h) * N + row) * D);
-  if (PH == 1) {
-    if (hh == 0 && row < N) {
-      park[0] = fbits(M);
-      park[1] = fbits(MN);
-    }
-    return;
-  }
-  if (PH == 2) {
+  if (ANCH) {
+    const uint32_t* const park = (const uint32_t*)((const __bf16*)a.o + ((size_t)(b * a.H + h) * N + wr0) * D) + 2 * li;
     M = row < N ? bitsf(park[0]) : 0.0f;
     MN = row < N ? bitsf(park[1]) : 0.0f;
   }
@@ -616,6 +551,182 @@ __global__ __launch_bounds__(NW * 64, PH == 1 ? 4 : 2) void fwd_fp8(FwdArgs a) {
 #endif
 }
 
+// ---- row-extrema pre-pass with two row blocks per wave ----------------------------------
+// The same extrema as the pre-pass block of fwd_fp8 (the same MMAs in the same order, so the
+// same fp32 scores), but a wave owns RB = 2 blocks of 32 query rows: every K operand read from
+// LDS feeds two MMAs, which halves the LDS reads per MMA.  Scores of tile t+1 are issued before
+// the extrema of tile t are folded.  The extrema are parked in O where fwd_fp8 reads them.
+constexpr int XNW = 4;              // waves per workgroup
+constexpr int XRB = 2;              // 32-row blocks per wave
+constexpr int XBM = XNW * 32 * XRB;  // query rows per workgroup
+constexpr int XNB = 3;              // K tile buffers (K loads run XNB tiles ahead)
+constexpr int XOCC = 2;             // workgroups per CU the register budget is sized for
+
+template <int D, bool TMIN>
+__global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KC = D / 64;
+  constexpr int SK = D / 16 + 1;  // 16-byte slots per K row (odd: conflict-free column reads)
+  constexpr int KR = SK * 16, KT = BN * KR;
+  constexpr int KIW = (SK + XNW - 1) / XNW;
+  constexpr int NK_MIN = SK / XNW;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31, hh = lane >> 5;
+  int bh, qt;
+  map_block(a, bh, qt);
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int kvh = h / (a.H / a.Hkv);
+  const int N = a.N;
+  const int q0 = qt * XBM;
+  const int wr0 = q0 + wave * 32 * XRB;
+  const uint8_t* Qg = (const uint8_t*)a.q + (size_t)(b * a.H + h) * N * D;
+  const uint8_t* const Kg = (const uint8_t*)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
+
+  // Q^T operands, lane (li, hh) of block rb: Q[wr0 + 32 rb + li][64c + 32hh .. +31]
+  i32x8 qf[XRB][KC];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const int row = wr0 + 32 * rb + li;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+      if (row < N) {
+        lo = *(const u32x4*)(Qg + (size_t)row * D + 64 * c + 32 * hh);
+        hi = *(const u32x4*)(Qg + (size_t)row * D + 64 * c + 32 * hh + 16);
+      }
+      qf[rb][c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  }
+
+  const int T = a.causal ? ((min(q0 + XBM, N) - 1) / BN + 1) : (N + BN - 1) / BN;
+  int last[XRB];
+  bool lmask[XRB];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const int r0 = wr0 + 32 * rb;
+    last[rb] = r0 >= N ? -1 : (a.causal ? (min(r0 + 31, N - 1) / BN) : T - 1);
+    lmask[rb] = (a.causal && last[rb] * BN + BN - 1 > r0) || (last[rb] * BN + BN > N);
+  }
+  const int wlast = max(last[0], last[1]);
+
+  // K tiles: slot s (64 per wave instruction) is row s / SK, chunk s % SK; the pad chunk
+  // loads zeros from an out-of-range offset
+  uint32_t kvo[KIW];
+#pragma unroll
+  for (int m = 0; m < KIW; ++m) {
+    const int sl = (wave + XNW * m) * 64 + lane, j = sl / SK, c = sl % SK;
+    kvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+  }
+  auto load_k = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kt * BN * D), 0, (N - kt * BN) * D, 0x00020000);
+#pragma unroll
+    for (int m = 0; m < KIW; ++m)
+      if (wave + XNW * m < SK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + XNW * m) * 1024), 16, kvo[m], 0, 0, 0);
+  };
+
+  const uint32_t koff = li * KR + hh * 32;
+  const f32x16 zero16 = {};
+  // scores of tile buf for both row blocks: s[rb][kb] = 32 keys kb x 32 rows rb (S^T)
+  auto qk = [&](int buf, f32x16 (&s)[XRB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 lo = *(const lds_u32x4*)(kbase + 64 * c);
+        const u32x4 hi = *(const lds_u32x4*)(kbase + 64 * c + 16);
+        const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+        for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma8<0>(ka, qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+      }
+    }
+  };
+  float M[XRB], MN[XRB];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    M[rb] = -__builtin_inff();
+    MN[rb] = __builtin_inff();
+  }
+  auto fold = [&](int rb, const f32x16 (&s)[2], int kt, bool masked) {
+    const int row = wr0 + 32 * rb + li;
+    const int lim = a.causal ? min(row, N - 1) : N - 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = !masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim;
+        M[rb] = fmaxf(M[rb], ok ? s[kb][r] : -__builtin_inff());
+        if (TMIN) MN[rb] = fminf(MN[rb], ok ? s[kb][r] : __builtin_inff());
+      }
+  };
+  auto fold_all = [&](const f32x16 (&s)[XRB][2], int t) {
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) {
+      if (t < last[rb]) fold(rb, s[rb], t, false);
+      else if (t == last[rb]) fold(rb, s[rb], t, lmask[rb]);
+    }
+  };
+
+  for (int j = 0; j < XNB; ++j)
+    if (j < T) load_k(j, j);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 s[XRB][2];
+  if (wlast >= 0) qk(0, s);
+  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+  int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
+  for (int t = 0; t < T; ++t) {
+    if (t + XNB < T) load_k(t + XNB, kl);  // buffer of K(t), last read in iteration t-1
+    if (t < wlast) {
+      f32x16 sn[XRB][2];
+      qk(kn, sn);
+      fold_all(s, t);
+#pragma unroll
+      for (int rb = 0; rb < XRB; ++rb) {
+        s[rb][0] = sn[rb][0];
+        s[rb][1] = sn[rb][1];
+      }
+    } else if (t == wlast) {
+      fold_all(s, t);
+    }
+    // K(t+2) must have landed; K(t+3) (this iteration's loads) may still be in flight
+    if (XNB == 3 && t + 3 < T) {
+      if (wave < SK % XNW)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK_MIN + 1) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK_MIN) : "memory");
+      lds_barrier();
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    kl = kn;
+    kn = kn + 1 == XNB ? 0 : kn + 1;
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const float m = half_max(M[rb]);
+    const float mn = half_min(MN[rb]);
+    const int r0 = wr0 + 32 * rb;
+    // packed at the start of the 32-row block's slice of O, where fwd_fp8 reads them
+    uint32_t* const park = (uint32_t*)((__bf16*)a.o + ((size_t)bh * N + r0) * D) + 2 * li;
+    if (hh == 0 && r0 + li < N) {
+      park[0] = fbits(m);
+      park[1] = fbits(mn);
+    }
+  }
+#endif
+}
+
 template <int D, int WK>
 hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   FwdArgs a = a0;
@@ -626,28 +737,33 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   constexpr int SK = D / 16 + 1, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
   const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
-  constexpr int PHM = ANCH ? 2 : 0;  // phase of the main launch
   // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
   // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does
   const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
-  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false, PHM>
-                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8, PHM> : (const void*)fwd_fp8<D, WK, false, false, PHM>;
+  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false>
+                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8> : (const void*)fwd_fp8<D, WK, false, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if constexpr (ANCH) {  // the pre-pass needs only the K buffers
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false, 1>), dim3(a.total_blocks), dim3(NW * 64),
-                       (size_t)BN * NB * SK * 16, st, a);
+  if constexpr (ANCH) {  // the row-extrema pre-pass, on its own workgroup grid
+    FwdArgs x = a0;
+    x.n_qtiles = (x.N + XBM - 1) / XBM;
+    x.total_blocks = x.B * x.H * x.n_qtiles;
+    const size_t xl = (size_t)BN * XNB * SK * 16;  // K tile buffers only
+    if (x.track_min)
+      hipLaunchKernelGGL((rowext_fp8<D, true>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
+    else
+      hipLaunchKernelGGL((rowext_fp8<D, false>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else if (wide)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false, PHM>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
