@@ -72,9 +72,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr int KT = BN * KR, VT = BN * VR;
   constexpr int KIW = (SK + NW - 1) / NW;
   constexpr int VIW = (SV + NW - 1) / NW;
-  // PoT: K loads run three tiles ahead (three buffers) and V loads two (three buffers), so
-  // that a tile has a whole iteration to land.  The other kinds keep K two tiles ahead and a
-  // register-staged V one tile ahead (two buffers each), which measures faster for them.
+  // LDS tile buffers: PoT three each for K and V (its loop is described there); the other
+  // kinds keep K two tiles ahead and a register-staged V one tile ahead (two buffers each),
+  // which measures faster for them.
   constexpr int NKB = PV8 ? 3 : 2, NVB = PV8 ? 3 : 2;
   constexpr int VB0 = NKB * KT;
 
@@ -437,7 +437,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float l = 0.0f;
-  __syncthreads();  // pre-pass reads done before the buffers are refilled
   load_v(0, 0);
   for (int j = 0; j < NKB; ++j)
     if (j < T) load_k(j, j);
@@ -446,30 +445,80 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   if (PV8 && T > 1) load_v(1, 1);  // PoT: LDS-direct V loads run two tiles ahead too
   __syncthreads();  // also publishes the K-interval tables
   f32x16 s[2];
-  if (wlast >= 0) qk(0, s, init16);
-  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-  int kl = 0, kn = 1, vc = 0;  // buffers of K(t), K(t+1), V(t)
-  for (int t = 0; t < T; ++t) {
-    // Prefetch K(t+NKB) into the buffer of K(t) and (PoT) V(t+2) into that of V(t-1): both
-    // last read in iteration t-1.  A PoT wave that multiplies P by V this iteration issues
-    // them after its V reads (the compiler makes transposing LDS reads wait for every
-    // LDS-direct load issued before them); other waves and kinds issue them right away.
+  if constexpr (PV8) {
+    // PoT, software-pipelined one tile deeper: iteration t multiplies P(t) by V(t) while it
+    // forms the weights of tile t+1 and issues the scores of tile t+2, so the PV MMAs do not
+    // depend on this iteration's weight VALU work and are issued between its instructions
+    // (measured 2 % faster than forming P(t) and multiplying it in the same iteration).
+    // K and V tile j sit in LDS buffer j % 3.  Iteration t reads K(t+2) and V(t), and
+    // prefetches K(t+4) into the buffer of K(t+1) and V(t+2) into that of V(t-1), both last
+    // read in iteration t-1; at its end K(t+3) and V(t+1), issued one iteration earlier, must
+    // have landed.  The prefetch is issued after the V operand reads (the compiler makes
+    // transposing LDS reads wait for every LDS-direct load issued before them).
+    uint32_t P8c[8];  // weights of tile t, consumed by PV in iteration t
+    {
+      f32x16 s0[2];
+      if (wlast >= 0) qk(0, s0, init16);
+      if (wlast >= 1) qk(1, s, init16);
+      __syncthreads();  // every wave has read K(0) and K(1) before their buffers are refilled
+      if (3 < T) load_k(3, 0);  // with V(1), the loads iteration -1 would have issued
+      if (wlast >= 0) weights8(s0, P8c, 0, wlast == 0 && last_masked);
+    }
+    int c0 = 0, c1 = 1, c2 = 2;  // t % 3, (t+1) % 3, (t+2) % 3
+    int t = 0;
     auto prefetch = [&]() {
-      if (t + NKB < T) load_k(t + NKB, kl);
-      if (PV8 && t + 2 < T) load_v(t + 2, vc == 0 ? 2 : vc - 1);
+      if (t + 4 < T) load_k(t + 4, c1);
+      if (t + 2 < T) load_v(t + 2, c2);
     };
-    if (!PV8 || t > wlast) prefetch();
-    if (!PV8 && t + 1 < T) load_v(t + 1, (t + 1) & 1);  // register-staged, widened at the end
-    if (t < wlast) {
-      if (PV8) {
-        const f32x16 sn0 = qk1(kn, 0, init16);
-        uint32_t P8[8];
-        weights8(s, P8, t, false);
-        const f32x16 sn1 = qk1(kn, 1, init16);
-        pv8(vc, P8, o, prefetch);
-        s[0] = sn0;
-        s[1] = sn1;
+    auto end_iteration = [&]() {
+      // K(t+3) and V(t+1) must have landed; this iteration's K(t+4) and V(t+2) may not have
+      if (t + 4 < T) {
+        if (wave < SK % NW)
+          loads_done_but(std::integral_constant<int, NK_MIN + 1 + NV_MIN>());
+        else
+          loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
+      } else if (t + 2 < T)
+        loads_done_but(std::integral_constant<int, NV_MIN>());
+      else
+        loads_done();
+      lds_barrier();
+      c0 = c1;
+      c1 = c2;
+      c2 = c2 + 1 == 3 ? 0 : c2 + 1;
+    };
+    // steady state: tiles t, t+1 and t+2 all hold visible keys, none needs masking
+    for (; t + 2 <= wlast; ++t) {
+      pv8(c0, P8c, o, prefetch);
+      const f32x16 sn0 = qk1(c2, 0, init16);
+      weights8(s, P8c, t + 1, false);
+      const f32x16 sn1 = qk1(c2, 1, init16);
+      s[0] = sn0;
+      s[1] = sn1;
+      end_iteration();
+    }
+    // the last two tiles of this wave (the last may need masking), then the iterations in
+    // which the wave only issues its share of the other waves' tile loads
+    for (; t < T; ++t) {
+      if (t + 1 == wlast) {
+        pv8(c0, P8c, o, prefetch);
+        weights8(s, P8c, t + 1, last_masked);
+      } else if (t == wlast) {
+        pv8(c0, P8c, o, prefetch);
       } else {
+        prefetch();
+      }
+      end_iteration();
+    }
+  } else {
+    // exact and K-interval: K two tiles ahead in two LDS buffers, V one tile ahead through
+    // registers (widened to bf16 into the other V buffer at the end of the iteration)
+    if (wlast >= 0) qk(0, s, init16);
+    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+    int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
+    for (int t = 0; t < T; ++t) {
+      if (t + NKB < T) load_k(t + NKB, kl);  // buffer of K(t), last read in iteration t-1
+      if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
+      if (t < wlast) {
         const f32x16 sn0 = qk1(kn, 0, init16);
         if (WK == WK_EXACT) online_max(s, o, l);
         u32x4 P[2];
@@ -480,13 +529,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         pv1(t & 1, 1, P, o);
         s[0] = sn0;
         s[1] = sn1;
-      }
-    } else if (t == wlast) {
-      if (PV8) {
-        uint32_t P8[8];
-        weights8(s, P8, t, last_masked);
-        pv8(vc, P8, o, prefetch);
-      } else {
+      } else if (t == wlast) {
         if (WK == WK_EXACT) {
           f32x16 sm[2] = {s[0], s[1]};
           if (last_masked) mask_fill(sm, t, -__builtin_inff());
@@ -498,27 +541,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         weights16(s[1], 1, P, l, t, last_masked);
         pv1(t & 1, 1, P, o);
       }
-    }
-    if (PV8) {
-      // K(t+2) and V(t+1), loaded last iteration, have landed; this iteration's may not have
-      if (t + 3 < T) {
-        if (wave < SK % NW)
-          loads_done_but(std::integral_constant<int, NK_MIN + 1 + NV_MIN>());
-        else
-          loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
-      } else if (t + 2 < T)
-        loads_done_but(std::integral_constant<int, NV_MIN>());
-      else
-        loads_done();
-      lds_barrier();
-    } else {
       loads_done();
-      if (t + 1 < T) store_v((t + 1) & 1);  // register-staged V, widened to bf16
+      if (t + 1 < T) store_v((t + 1) & 1);
       __syncthreads();
+      kl = kn;
+      kn = kn + 1 == NKB ? 0 : kn + 1;
     }
-    kl = kn;
-    kn = kn + 1 == NKB ? 0 : kn + 1;
-    vc = vc + 1 == NVB ? 0 : vc + 1;
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -559,7 +587,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 constexpr int XNW = 4;              // waves per workgroup
 constexpr int XRB = 2;              // 32-row blocks per wave
 constexpr int XBM = XNW * 32 * XRB;  // query rows per workgroup
-constexpr int XNB = 3;              // K tile buffers (K loads run XNB tiles ahead)
+constexpr int XNB = 2;              // K tile buffers (K loads run XNB tiles ahead; 2 measured 1 % faster than 3)
 constexpr int XOCC = 2;             // workgroups per CU the register budget is sized for
 
 template <int D, bool TMIN>
@@ -697,7 +725,8 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
     } else if (t == wlast) {
       fold_all(s, t);
     }
-    // K(t+2) must have landed; K(t+3) (this iteration's loads) may still be in flight
+    // K(t+2) must have landed: with two buffers it is this iteration's load; with three,
+    // this iteration's K(t+3) may stay in flight
     if (XNB == 3 && t + 3 < T) {
       if (wave < SK % XNW)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK_MIN + 1) : "memory");
