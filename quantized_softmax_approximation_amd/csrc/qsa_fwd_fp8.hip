@@ -603,7 +603,7 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
   lds_u8* const lds = (lds_u8*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int li = lane & 31, hh = lane >> 5;
   int bh, qt;
   map_block(a, bh, qt);
@@ -634,11 +634,13 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
   const int T = a.causal ? ((min(q0 + XBM, N) - 1) / BN + 1) : (N + BN - 1) / BN;
   int last[XRB];
   bool lmask[XRB];
+  int tclean = T;  // tiles t < tclean are visible and unmasked for every row block of the wave
 #pragma unroll
   for (int rb = 0; rb < XRB; ++rb) {
     const int r0 = wr0 + 32 * rb;
     last[rb] = r0 >= N ? -1 : (a.causal ? (min(r0 + 31, N - 1) / BN) : T - 1);
     lmask[rb] = (a.causal && last[rb] * BN + BN - 1 > r0) || (last[rb] * BN + BN > N);
+    tclean = min(tclean, lmask[rb] ? last[rb] : last[rb] + 1);
   }
   const int wlast = max(last[0], last[1]);
 
@@ -711,20 +713,8 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
   if (wlast >= 0) qk(0, s);
   __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
   int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
-  for (int t = 0; t < T; ++t) {
-    if (t + XNB < T) load_k(t + XNB, kl);  // buffer of K(t), last read in iteration t-1
-    if (t < wlast) {
-      f32x16 sn[XRB][2];
-      qk(kn, sn);
-      fold_all(s, t);
-#pragma unroll
-      for (int rb = 0; rb < XRB; ++rb) {
-        s[rb][0] = sn[rb][0];
-        s[rb][1] = sn[rb][1];
-      }
-    } else if (t == wlast) {
-      fold_all(s, t);
-    }
+  int t = 0;
+  auto end_iteration = [&]() {
     // K(t+2) must have landed: with two buffers it is this iteration's load; with three,
     // this iteration's K(t+3) may stay in flight
     if (XNB == 3 && t + 3 < T) {
@@ -739,6 +729,49 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
     }
     kl = kn;
     kn = kn + 1 == XNB ? 0 : kn + 1;
+  };
+  // steady state: tile t is unmasked for both row blocks and tile t+1 is needed.  Unrolled
+  // by two so that the score sets swap roles instead of being copied.
+  auto step = [&](const f32x16 (&cur)[XRB][2], f32x16 (&nxt)[XRB][2]) {
+    if (t + XNB < T) load_k(t + XNB, kl);  // buffer of K(t), last read in iteration t-1
+    qk(kn, nxt);
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) fold(rb, cur[rb], t, false);
+    end_iteration();
+  };
+  f32x16 s2[XRB][2];
+  for (; t + 2 < tclean; t += 2) {
+    step(s, s2);
+    ++t;
+    step(s2, s);
+    --t;
+  }
+  if (t + 1 < tclean) {
+    step(s, s2);
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) {
+      s[rb][0] = s2[rb][0];
+      s[rb][1] = s2[rb][1];
+    }
+    ++t;
+  }
+  // the remaining tiles of the wave (masked or past a row block's last), then the iterations
+  // in which it only issues its share of the other waves' tile loads
+  for (; t < T; ++t) {
+    if (t + XNB < T) load_k(t + XNB, kl);
+    if (t < wlast) {
+      f32x16 sn[XRB][2];
+      qk(kn, sn);
+      fold_all(s, t);
+#pragma unroll
+      for (int rb = 0; rb < XRB; ++rb) {
+        s[rb][0] = sn[rb][0];
+        s[rb][1] = sn[rb][1];
+      }
+    } else if (t == wlast) {
+      fold_all(s, t);
+    }
+    end_iteration();
   }
 
 #pragma unroll
