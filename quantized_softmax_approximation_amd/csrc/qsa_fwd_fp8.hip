@@ -43,6 +43,15 @@ __device__ __forceinline__ int vswz_of(int r) {
   return D == 128 ? 2 * (((r >> 1) & 1) | ((r >> 2) & 2)) : 2 * ((r >> 3) & 1);
 }
 
+// Slot of 16-byte chunk q of K row r is q ^ kswz(r).  A ds_read_b128 of the score loop reads
+// the same chunk of 32 consecutive rows; with unpadded 128-byte (d = 128) or 64-byte rows the
+// XOR puts every 16-row lane group, and every 8-row half of one, on distinct LDS bank groups
+// (rows r and r + 32 share the swizzle).
+template <int D>
+__device__ __forceinline__ int kswz_of(int r) {
+  return D == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
+}
+
 // v_pk_mad_u16: a * b + c in each 16-bit half
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
@@ -65,12 +74,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
   constexpr bool PV8 = POT;
-  constexpr int SK = D / 16 + 1;                      // 16-byte slots per K row (odd)
+  constexpr int SK = D / 16;                          // 16-byte slots per K row (swizzled)
   constexpr int SV = PV8 ? D / 16 : (D / 8 + 4);  // fp8 V rows (swizzled, unpadded), or bf16 rows (stride 64 mod 256)
   constexpr int KR = SK * 16, VR = SV * 16;
   auto vswz = [](int r) { return vswz_of<D>(r); };
   constexpr int KT = BN * KR, VT = BN * VR;
-  constexpr int KIW = (SK + NW - 1) / NW;
+  constexpr int KIW = SK / NW;  // K-tile load instructions per wave
+  static_assert(SK % NW == 0, "K tiles split evenly over the waves");
   constexpr int VIW = (SV + NW - 1) / NW;
   // LDS tile buffers: PoT three each for K and V (its loop is described there); the other
   // kinds keep K two tiles ahead and a register-staged V one tile ahead (two buffers each),
@@ -119,13 +129,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 
   // ---- tile staging ------------------------------------------------------
   // K (and V for PoT): buffer loads straight into LDS, 64 consecutive 16-byte
-  // slots per wave-instruction; slot s is row s / S, chunk s % S (pad chunks
-  // load zeros from an out-of-range offset).
+  // slots per wave-instruction; K slot s is row j = s / SK, slot s % SK of the row, which
+  // holds chunk (s % SK) ^ kswz(j).
   uint32_t kvo[KIW];
 #pragma unroll
   for (int m = 0; m < KIW; ++m) {
-    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK, c = sl % SK;
-    kvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK;
+    kvo[m] = (uint32_t)(j * D + ((sl % SK) ^ kswz_of<D>(j)) * 16);
   }
   auto tile_rsrc = [&](const uint8_t* base, int kt) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D, 0x00020000);
@@ -134,9 +144,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kg, kt);
 #pragma unroll
     for (int m = 0; m < KIW; ++m)
-      if (wave + NW * m < SK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + off + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + off + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
   };
   auto load_k = [&](int kt, int buf) { load_k_at(kt, buf * KT); };
   uint32_t vvo[PV8 ? VIW : 1];
@@ -201,15 +210,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
   };
 
-  // QK operand reads: lane (li, hh), k-step c: 32 bytes of K row li at 64c + 32hh
-  const uint32_t koff = li * KR + hh * 32;
+  // QK operand reads: lane (li, hh), k-step c: chunks 4c + 2hh and 4c + 2hh + 1 of K row li
+  // (32 bytes), at their swizzled slots
+  uint32_t koff[KC][2];
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[c][u] = li * KR + 16 * ((4 * c + 2 * hh + u) ^ kswz_of<D>(li));
   auto qk1 = [&](int buf, int kb, const f32x16& init) {
-    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
+    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR;
     f32x16 s = init;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 lo = *(const lds_u32x4*)(kbase + 64 * c);
-      const u32x4 hi = *(const lds_u32x4*)(kbase + 64 * c + 16);
+      const u32x4 lo = *(const lds_u32x4*)(kbase + koff[c][0]);
+      const u32x4 hi = *(const lds_u32x4*)(kbase + koff[c][1]);
       const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       s = mma8<0>(ka, qf[c], c == 0 ? init : s);
     }
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     if (j < T) load_k(j, j);
   loads_done();
   store_v(0);
-  if (PV8 && T > 1) load_v(1, 1);  // PoT: LDS-direct V loads run two tiles ahead too
+  if (PV8) load_v(min(1, T - 1), 1);  // PoT: LDS-direct V loads run two tiles ahead too
   __syncthreads();  // also publishes the K-interval tables
   f32x16 s[2];
   if constexpr (PV8) {
@@ -461,26 +475,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       if (wlast >= 0) qk(0, s0, init16);
       if (wlast >= 1) qk(1, s, init16);
       __syncthreads();  // every wave has read K(0) and K(1) before their buffers are refilled
-      if (3 < T) load_k(3, 0);  // with V(1), the loads iteration -1 would have issued
+      load_k(min(3, T - 1), 0);  // with V(1), the loads iteration -1 would have issued
       if (wlast >= 0) weights8(s0, P8c, 0, wlast == 0 && last_masked);
     }
     int c0 = 0, c1 = 1, c2 = 2;  // t % 3, (t+1) % 3, (t+2) % 3
     int t = 0;
+    // Every iteration issues the same loads, so that neither the prefetch nor the wait needs a
+    // branch: past the last tile it reloads tile T-1 into a buffer no later iteration reads
+    // (K(t+4) would be read in iteration t+2 only if t+4 <= wlast, V(t+2) in iteration t+2).
     auto prefetch = [&]() {
-      if (t + 4 < T) load_k(t + 4, c1);
-      if (t + 2 < T) load_v(t + 2, c2);
+      load_k(min(t + 4, T - 1), c1);
+      load_v(min(t + 2, T - 1), c2);
     };
     auto end_iteration = [&]() {
-      // K(t+3) and V(t+1) must have landed; this iteration's K(t+4) and V(t+2) may not have
-      if (t + 4 < T) {
-        if (wave < SK % NW)
-          loads_done_but(std::integral_constant<int, NK_MIN + 1 + NV_MIN>());
-        else
-          loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
-      } else if (t + 2 < T)
-        loads_done_but(std::integral_constant<int, NV_MIN>());
-      else
-        loads_done();
+      // K(t+3) and V(t+1) must have landed; this iteration's loads may still be in flight
+      loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
       lds_barrier();
       c0 = c1;
       c1 = c2;
@@ -509,6 +518,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       }
       end_iteration();
     }
+    loads_done();  // no LDS-direct load outlives the workgroup
   } else {
     // exact and K-interval: K two tiles ahead in two LDS buffers, V one tile ahead through
     // registers (widened to bf16 into the other V buffer at the end of the iteration)
@@ -594,10 +604,10 @@ template <int D, bool TMIN>
 __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = D / 64;
-  constexpr int SK = D / 16 + 1;  // 16-byte slots per K row (odd: conflict-free column reads)
+  constexpr int SK = D / 16;  // 16-byte slots per K row (swizzled as in fwd_fp8)
   constexpr int KR = SK * 16, KT = BN * KR;
-  constexpr int KIW = (SK + XNW - 1) / XNW;
-  constexpr int NK_MIN = SK / XNW;
+  constexpr int KIW = SK / XNW;  // K-tile load instructions per wave
+  static_assert(SK % XNW == 0, "K tiles split evenly over the waves");
 
   extern __shared__ __align__(16) unsigned char smem[];
   lds_u8* const lds = (lds_u8*)smem;
@@ -644,35 +654,38 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
   }
   const int wlast = max(last[0], last[1]);
 
-  // K tiles: slot s (64 per wave instruction) is row s / SK, chunk s % SK; the pad chunk
-  // loads zeros from an out-of-range offset
+  // K tiles: slot s (64 per wave instruction) is row j = s / SK, slot s % SK of the row,
+  // which holds chunk (s % SK) ^ kswz(j)
   uint32_t kvo[KIW];
 #pragma unroll
   for (int m = 0; m < KIW; ++m) {
-    const int sl = (wave + XNW * m) * 64 + lane, j = sl / SK, c = sl % SK;
-    kvo[m] = c < D / 16 ? (uint32_t)(j * D + c * 16) : 0x7FFFFFF0u;
+    const int sl = (wave + XNW * m) * 64 + lane, j = sl / SK;
+    kvo[m] = (uint32_t)(j * D + ((sl % SK) ^ kswz_of<D>(j)) * 16);
   }
   auto load_k = [&](int kt, int buf) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kt * BN * D), 0, (N - kt * BN) * D, 0x00020000);
 #pragma unroll
     for (int m = 0; m < KIW; ++m)
-      if (wave + XNW * m < SK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + XNW * m) * 1024), 16, kvo[m], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + XNW * m) * 1024), 16, kvo[m], 0, 0, 0);
   };
 
-  const uint32_t koff = li * KR + hh * 32;
+  uint32_t koff[KC][2];  // chunks 4c + 2hh (+1) of K row li at their swizzled slots
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[c][u] = li * KR + 16 * ((4 * c + 2 * hh + u) ^ kswz_of<D>(li));
   const f32x16 zero16 = {};
   // scores of tile buf for both row blocks: s[rb][kb] = 32 keys kb x 32 rows rb (S^T)
   auto qk = [&](int buf, f32x16 (&s)[XRB][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
+      const lds_u8* kbase = lds + buf * KT + kb * 32 * KR;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const u32x4 lo = *(const lds_u32x4*)(kbase + 64 * c);
-        const u32x4 hi = *(const lds_u32x4*)(kbase + 64 * c + 16);
+        const u32x4 lo = *(const lds_u32x4*)(kbase + koff[c][0]);
+        const u32x4 hi = *(const lds_u32x4*)(kbase + koff[c][1]);
         const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
         for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma8<0>(ka, qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
@@ -718,10 +731,7 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
     // K(t+2) must have landed: with two buffers it is this iteration's load; with three,
     // this iteration's K(t+3) may stay in flight
     if (XNB == 3 && t + 3 < T) {
-      if (wave < SK % XNW)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK_MIN + 1) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK_MIN) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KIW) : "memory");
       lds_barrier();
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -796,7 +806,7 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   a.total_blocks = a.B * a.H * a.n_qtiles;
   constexpr bool PV8 = (WK == WK_POT || WK == WK_POT_FLUSH);
   constexpr bool ANCH = WK != WK_EXACT;
-  constexpr int SK = D / 16 + 1, SV = PV8 ? D / 16 : (D / 8 + 4);
+  constexpr int SK = D / 16, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
   const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
   // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
