@@ -165,11 +165,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
     if (PV8) {
 #pragma unroll
-      for (int m = 0; m < VIW; ++m)
-        if (wave + NW * m < SV)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              r, (__attribute__((address_space(3))) void*)(lds + VB0 + buf * VT + (wave + NW * m) * 1024), 16,
-              vvo[m], 0, 0, 0);
+      for (int m = 0; m < VIW; ++m)  // SV % NW == 0: every wave issues VIW of them
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + VB0 + buf * VT + (wave + NW * m) * 1024), 16,
+            vvo[m], 0, 0, 0);
     } else {
 #pragma unroll
       for (int m = 0; m < VQL; ++m)
@@ -217,7 +216,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   for (int c = 0; c < KC; ++c)
 #pragma unroll
     for (int u = 0; u < 2; ++u) koff[c][u] = li * KR + 16 * ((4 * c + 2 * hh + u) ^ kswz_of<D>(li));
-  auto qk1 = [&](int buf, int kb, const f32x16& init) {
+  auto qk1 = [&](int buf, int kb, const f32x16& init) __attribute__((always_inline)) {
     const lds_u8* kbase = lds + buf * KT + kb * 32 * KR;
     f32x16 s = init;
 #pragma unroll
@@ -269,11 +268,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   const int sel = (((lane & 15) < 8) == (((lane >> 4) & 1) == 0)) ? 0x38383838 : 0;
   const i32x8 rs_sel = {sel, sel, sel, sel, sel, sel, sel, sel};
   f32x4 rs = {0.0f, 0.0f, 0.0f, 0.0f};  // PoT row sums (see the epilogue for the layout)
-  // mid() runs after the V operand reads are issued and before the MMAs
-  auto pv8 = [&](int buf, const uint32_t (&P8)[8], f32x16 (&o)[DB], auto&& mid) {
+  // V^T operands of the V tile in LDS buffer buf
+  auto read_v8 = [&](int buf, i32x8 (&va)[DB]) __attribute__((always_inline)) {
     const lds_u8* vbase = lds + VB0 + buf * VT;
-    const i32x8 pb = {(int)P8[0], (int)P8[1], (int)P8[2], (int)P8[3], (int)P8[4], (int)P8[5], (int)P8[6], (int)P8[7]};
-    i32x8 va[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -282,7 +279,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         va[db][2 * k] = v2[0];
         va[db][2 * k + 1] = v2[1];
       }
-    mid();
+  };
+  // O^T += V^T P^T and the row-sum MMA
+  auto mma_pv8 = [&](const i32x8 (&va)[DB], const uint32_t (&P8)[8], f32x16 (&o)[DB]) __attribute__((always_inline)) {
+    const i32x8 pb = {(int)P8[0], (int)P8[1], (int)P8[2], (int)P8[3], (int)P8[4], (int)P8[5], (int)P8[6], (int)P8[7]};
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = mma8<1>(va[db], pb, o[db]);
     rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rs_sel, pb, rs, 0, 1, 0, 0, 0, 0);
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // pairs (-e0, -e1) and (-e2, -e3) become the bytes 4(L - e) in the order r0, r0+2, r0+1,
   // r0+3 by two v_pk_mad_u16: 4(-e) + 4L*257 gives byte 0 and a carry-free 4L in byte 1 of
   // each half, then 1024(-e') adds the second pair's bytes in byte 1.
-  auto weights8 = [&](const f32x16 (&s)[2], uint32_t (&P8)[8], int kt, bool masked) {
+  auto weights8 = [&](const f32x16 (&s)[2], uint32_t (&P8)[8], int kt, bool masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r0 = 4 * (w & 3);
@@ -452,71 +452,91 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float l = 0.0f;
   load_v(0, 0);
+  if (PV8) load_v(min(1, T - 1), 1);  // PoT: V(1) is read before the loop's first barrier
   for (int j = 0; j < NKB; ++j)
     if (j < T) load_k(j, j);
   loads_done();
   store_v(0);
-  if (PV8) load_v(min(1, T - 1), 1);  // PoT: LDS-direct V loads run two tiles ahead too
   __syncthreads();  // also publishes the K-interval tables
   f32x16 s[2];
   if constexpr (PV8) {
-    // PoT, software-pipelined one tile deeper: iteration t multiplies P(t) by V(t) while it
-    // forms the weights of tile t+1 and issues the scores of tile t+2, so the PV MMAs do not
-    // depend on this iteration's weight VALU work and are issued between its instructions
-    // (measured 2 % faster than forming P(t) and multiplying it in the same iteration).
-    // K and V tile j sit in LDS buffer j % 3.  Iteration t reads K(t+2) and V(t), and
-    // prefetches K(t+4) into the buffer of K(t+1) and V(t+2) into that of V(t-1), both last
-    // read in iteration t-1; at its end K(t+3) and V(t+1), issued one iteration earlier, must
-    // have landed.  The prefetch is issued after the V operand reads (the compiler makes
-    // transposing LDS reads wait for every LDS-direct load issued before them).
+    // PoT, software-pipelined: iteration t multiplies P(t) by V(t) while it reads the V
+    // operands of tile t+1, forms the weights of tile t+1 and issues the scores of tile t+2.
+    // The PV MMAs then depend on nothing this iteration computes or reads: they are issued
+    // between its weight VALU instructions (2 % faster than forming P(t) and multiplying it
+    // in one iteration) and do not wait for the latency of their V reads (2 % faster than
+    // reading V(t) in iteration t).  K and V tile j sit in LDS buffer j % 3.  Iteration t
+    // reads K(t+2) and V(t+1), and prefetches K(t+4) into the buffer of K(t+1) and V(t+3)
+    // into that of V(t), both last read in iteration t-1; at its end K(t+3) and V(t+2),
+    // issued one iteration earlier, must have landed.  The prefetch is issued after the V
+    // operand reads (the compiler makes transposing LDS reads wait for every LDS-direct load
+    // issued before them).
     uint32_t P8c[8];  // weights of tile t, consumed by PV in iteration t
+    i32x8 va[DB];     // V operands of tile t, consumed by PV in iteration t
     {
       f32x16 s0[2];
-      if (wlast >= 0) qk(0, s0, init16);
+      if (wlast >= 0) {
+        qk(0, s0, init16);
+        read_v8(0, va);
+      }
       if (wlast >= 1) qk(1, s, init16);
-      __syncthreads();  // every wave has read K(0) and K(1) before their buffers are refilled
-      load_k(min(3, T - 1), 0);  // with V(1), the loads iteration -1 would have issued
+      __syncthreads();  // every wave has read K(0) before its buffer is refilled
+      // the loads iteration -1 would have issued
+      load_k(min(3, T - 1), 0);
+      load_v(min(2, T - 1), 2);
       if (wlast >= 0) weights8(s0, P8c, 0, wlast == 0 && last_masked);
     }
-    int c0 = 0, c1 = 1, c2 = 2;  // t % 3, (t+1) % 3, (t+2) % 3
     int t = 0;
     // Every iteration issues the same loads, so that neither the prefetch nor the wait needs a
     // branch: past the last tile it reloads tile T-1 into a buffer no later iteration reads
-    // (K(t+4) would be read in iteration t+2 only if t+4 <= wlast, V(t+2) in iteration t+2).
-    auto prefetch = [&]() {
-      load_k(min(t + 4, T - 1), c1);
-      load_v(min(t + 2, T - 1), c2);
+    // (K(t+4) and V(t+3) would be read in iteration t+2, only if t+4 <= wlast or t+3 <= wlast).
+    auto prefetch_to = [&](int b0, int b1) {
+      load_k(min(t + 4, T - 1), b1);
+      load_v(min(t + 3, T - 1), b0);
     };
-    auto end_iteration = [&]() {
-      // K(t+3) and V(t+1) must have landed; this iteration's loads may still be in flight
+    auto wait_tiles = [&]() {
+      // K(t+3) and V(t+2) must have landed; this iteration's loads may still be in flight
       loads_done_but(std::integral_constant<int, NK_MIN + NV_MIN>());
       lds_barrier();
-      c0 = c1;
-      c1 = c2;
-      c2 = c2 + 1 == 3 ? 0 : c2 + 1;
     };
     // steady state: tiles t, t+1 and t+2 all hold visible keys, none needs masking
-    for (; t + 2 <= wlast; ++t) {
-      pv8(c0, P8c, o, prefetch);
-      const f32x16 sn0 = qk1(c2, 0, init16);
+    auto steady = [&](int b0, int b1, int b2) __attribute__((always_inline)) {
+      mma_pv8(va, P8c, o);
+      read_v8(b1, va);
+      prefetch_to(b0, b1);
+      const f32x16 sn0 = qk1(b2, 0, init16);
       weights8(s, P8c, t + 1, false);
-      const f32x16 sn1 = qk1(c2, 1, init16);
+      const f32x16 sn1 = qk1(b2, 1, init16);
       s[0] = sn0;
       s[1] = sn1;
-      end_iteration();
+      wait_tiles();
+    };
+    // (unrolling this loop by three, which makes every LDS address a constant, measured the same)
+    int b0 = 0, b1 = 1, b2 = 2;  // t % 3, (t+1) % 3, (t+2) % 3
+    for (; t + 2 <= wlast; ++t) {
+      steady(b0, b1, b2);
+      b0 = b1;
+      b1 = b2;
+      b2 = b2 + 1 == 3 ? 0 : b2 + 1;
     }
     // the last two tiles of this wave (the last may need masking), then the iterations in
     // which the wave only issues its share of the other waves' tile loads
     for (; t < T; ++t) {
       if (t + 1 == wlast) {
-        pv8(c0, P8c, o, prefetch);
+        mma_pv8(va, P8c, o);
+        read_v8(b1, va);
+        prefetch_to(b0, b1);
         weights8(s, P8c, t + 1, last_masked);
       } else if (t == wlast) {
-        pv8(c0, P8c, o, prefetch);
+        mma_pv8(va, P8c, o);
+        prefetch_to(b0, b1);
       } else {
-        prefetch();
+        prefetch_to(b0, b1);
       }
-      end_iteration();
+      wait_tiles();
+      b0 = b1;
+      b1 = b2;
+      b2 = b2 + 1 == 3 ? 0 : b2 + 1;
     }
     loads_done();  // no LDS-direct load outlives the workgroup
   } else {
