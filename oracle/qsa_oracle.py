@@ -29,6 +29,14 @@ with three kinds of weight function w(s) replacing exp(s - m):
   "Row max -> Power-of-two weights"): a coarse logarithmic weight anchored at
   the row maximum.  With y = (m_i - s) * log2(e), e = rint(y) clipped to the
   stated level count L, w = 2**-e.
+* ``trunc`` and ``uniform`` -- the two operators of the sensitivity study on
+  the same "Approximating Softmax" page (abstract): the softmax support can be
+  cut to the scores close to the row maximum with little loss, while giving
+  the kept positions equal weight hurts.  Both keep the support
+  {j visible : s_ij >= m_i - W} for a window W; ``trunc`` gives the kept keys
+  their exact weights exp(s - m_i), ``uniform`` gives each of them weight 1,
+  so O_i is the plain mean of the kept values.  Keys outside the support get
+  weight 0 (index code 254, like a flushed element).
 
 Readings taken where the pages are silent (every one is listed in the design
 notes of the repository with its reason):
@@ -99,8 +107,14 @@ def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def _check_kind(kind, levels, window, interp, flush):
-    if kind not in ("exact", "kint", "pot"):
+    if kind not in ("exact", "kint", "pot", "trunc", "uniform"):
         raise ValueError(f"unknown kind {kind!r}")
+    if kind in ("trunc", "uniform"):
+        if window is None or not (window > 0 and math.isfinite(window)):
+            raise ValueError(f"{kind} needs a finite window W > 0")
+        if interp or flush:
+            raise ValueError(f"{kind} takes no interpolation or flush option")
+        return
     if kind == "kint" and not (isinstance(levels, int) and levels >= 1):
         raise ValueError("kint needs levels = K >= 1 intervals")
     if kind == "pot" and not (isinstance(levels, int) and levels >= 1):
@@ -138,6 +152,19 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
         w = np.where(visible, np.exp(np.where(visible, S - m[:, None], 0.0)), 0.0)
         idx[visible] = 0
         out.update(w=w, idx=idx, y=y, lo=mn, delta=np.zeros(R))
+        return out
+
+    if kind in ("trunc", "uniform"):
+        # support: the visible keys whose score is at least m - W (the row max is always kept)
+        kept = visible & (m[:, None] - S <= window)
+        if kind == "trunc":
+            w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)
+        else:
+            w = kept.astype(np.float64)
+        idx[kept] = 0
+        idx[visible & ~kept] = IDX_FLUSHED
+        y = np.where(visible, (m[:, None] - S) / window, np.nan)   # the support edge is y = 1
+        out.update(w=w, idx=idx, y=y, lo=m - window, delta=np.full(R, float(window)))
         return out
 
     if kind == "pot":

@@ -13,7 +13,10 @@ Definitions followed (readings as in the vectorised oracle):
   interpolation) and chapter 1 (exponential read off a grid calibrated per row);
   Rowmax-PoT -- "Approximating Softmax in Pretrained LLMs: Model Sensitivity
   and Kernel Acceleration", abstract (power-of-two weights anchored at each
-  row maximum).
+  row maximum);
+  support truncation and uniform weighting -- the same abstract's sensitivity
+  study (keep only the scores within W of the row maximum, with their exact
+  weights or with equal weights).
 """
 from __future__ import annotations
 
@@ -43,6 +46,15 @@ def weight_row(scores, visible, kind, levels=None, window=None, interp=False, fl
     if kind == "exact":
         for s, ok in zip(scores, visible):
             out.append(math.exp(s - m) if ok else 0.0)
+        return out
+    if kind in ("trunc", "uniform"):
+        for s, ok in zip(scores, visible):
+            if not ok or s < m - window:
+                out.append(0.0)
+            elif kind == "trunc":
+                out.append(math.exp(s - m))
+            else:
+                out.append(1.0)
         return out
     if kind == "pot":
         L = levels

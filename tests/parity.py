@@ -58,6 +58,9 @@ def _edges(var, y, K):
     kind = var["kind"]
     if kind == "exact":
         return np.full_like(y, np.inf), np.full_like(y, np.inf)
+    if kind in ("trunc", "uniform"):                             # the support edge y = (m - s)/W = 1
+        d = np.abs(y - 1.0)
+        return d, d
     frac_half = np.abs(y - np.floor(y) - 0.5)                   # distance to a half-integer
     if kind == "pot" or not var.get("interp", False):
         d_w = frac_half
@@ -77,6 +80,8 @@ def _eps(var, y, m, S, dstar, delta):
     base = 4 * U * (np.abs(m)[:, None] + np.abs(S))
     if kind == "pot":
         return (2 * dstar[:, None] + base) * LOG2E + 4 * U * np.abs(y)
+    if kind in ("trunc", "uniform"):
+        return (2 * dstar[:, None] + base) / var["window"] + 4 * U * np.abs(y)
     K = var["levels"]
     grow = 0.0 if var.get("window") is not None else (np.abs(y) / K)
     dd = np.where(delta > 0, delta, np.inf)[:, None]
@@ -86,6 +91,9 @@ def _eps(var, y, m, S, dstar, delta):
 def _other_weight(var, idx, y, T):
     """Weight an ambiguous element gets if it lands across its nearest edge."""
     kind = var["kind"]
+    if kind in ("trunc", "uniform"):   # across the support edge: cut if kept, kept if cut
+        inside = np.exp(-y * var["window"]) if kind == "trunc" else np.ones_like(y)
+        return np.where(y <= 1.0, 0.0, inside)
     fl = np.floor(y)
     other = np.where(y - fl < 0.5, fl + 1, fl)          # index across the nearest half-integer
     if kind == "pot":

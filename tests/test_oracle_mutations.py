@@ -40,6 +40,12 @@ MUTATIONS = {
     "missing_scale": ("S = sc * (qh[r] @ kh.T)", "S = (qh[r] @ kh.T)"),
     "gqa_wrong_head": ("kv = h // group", "kv = h % Hkv"),
     "flush_threshold": ("kept = visible & (e <= L - 1)", "kept = visible & (e <= L)"),
+    "support_edge_exclusive": ("kept = visible & (m[:, None] - S <= window)", "kept = visible & (m[:, None] - S < window)"),
+    "support_sign": ("kept = visible & (m[:, None] - S <= window)", "kept = visible & (S - m[:, None] <= window)"),
+    "uniform_takes_exact_weights": ("w = kept.astype(np.float64)",
+                                    "w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)"),
+    "trunc_takes_unit_weights": ("w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)\n        else:",
+                                 "w = kept.astype(np.float64)\n        else:"),
 }
 
 
@@ -83,6 +89,26 @@ def _checks(o):
                     r = o.attn_fwd(qq, kk, vv, causal=causal, **var)
                     rs = scalar.attention(qq[0, 0].tolist(), kk[0, 0].tolist(), vv[0, 0].tolist(), causal=causal, **var)
                     np.testing.assert_allclose(r["O"][0, 0], np.array(rs), atol=1e-12)
+        # sensitivity operators: the inclusive support edge on integer scores, then the closed forms
+        qe = np.array([[[[1.0, 0.0]]]])
+        ke = np.array([[[[5.0, 0.0], [3.0, 0.0], [2.0, 0.0], [4.0, 0.0]]]])
+        ve = np.array([[[[1.0, 0.0], [0.0, 1.0], [7.0, 7.0], [0.0, 0.0]]]])
+        for kind, w in (("trunc", [1.0, math.exp(-2.0), 0.0, math.exp(-1.0)]), ("uniform", [1.0, 1.0, 0.0, 1.0])):
+            r = o.attn_fwd(qe, ke, ve, kind=kind, window=2.0, scale=1.0)
+            w = np.array(w)
+            np.testing.assert_allclose(r["O"][0, 0, 0], (w @ ve[0, 0]) / w.sum(), atol=1e-15)
+        q = rng.standard_normal((1, 1, 10, 8)) * 1.3
+        k = rng.standard_normal((1, 1, 10, 8)) * 1.3
+        v = rng.standard_normal((1, 1, 10, 8))
+        S = (q[0, 0] @ k[0, 0].T) / math.sqrt(8)
+        P = torch.softmax(torch.from_numpy(S), dim=-1).numpy()
+        for W in (0.3, 1.2):
+            keep = S >= S.max(axis=1, keepdims=True) - W
+            ru = o.attn_fwd(q, k, v, kind="uniform", window=W)
+            np.testing.assert_allclose(ru["O"][0, 0], (keep @ v[0, 0]) / keep.sum(1, keepdims=True), atol=1e-13)
+            rt = o.attn_fwd(q, k, v, kind="trunc", window=W)
+            p = np.where(keep, P, 0.0)
+            np.testing.assert_allclose(rt["O"][0, 0], (p @ v[0, 0]) / p.sum(1, keepdims=True), atol=1e-13)
     except Exception:      # a failed assertion or a crash: either way the pins notice
         return False
     return True

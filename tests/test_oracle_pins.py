@@ -369,3 +369,91 @@ def test_sink_workload_boosts_key0_by_six():
     s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(128)
     # key 0's score sits about 6 above the others' mean in every row
     assert abs((s[..., 0].mean() - s[..., 1:].mean()) - 6.0) < 0.5
+
+
+# --------------------------------------------------------------------------- sensitivity operators
+# Support truncation and uniform weighting ("Approximating Softmax in Pretrained LLMs", abstract:
+# the support can be cut near the row maximum, equal weights on it hurt).  Pinned by closed forms.
+
+SUPPORT_OPS = [dict(kind="trunc", window=w) for w in (0.25, 1.5, 4.0)] + \
+              [dict(kind="uniform", window=w) for w in (0.25, 1.5, 4.0)]
+
+
+def _support(S_row, vis_row, W):
+    m = max(s for s, ok in zip(S_row, vis_row) if ok)
+    return [j for j, (s, ok) in enumerate(zip(S_row, vis_row)) if ok and s >= m - W]
+
+
+@pytest.mark.parametrize("var", SUPPORT_OPS, ids=lambda v: f"{v['kind']}-W{v['window']}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_support_ops_brute_force_scalar_agrees(var, causal):
+    for seed in range(6):
+        n = 3 + seed % 6
+        q, k, v = _rand_qkv(B=1, H=1, N=n, d=4, sigma=1.7, seed=300 + seed)
+        r = oracle.attn_fwd(q, k, v, causal=causal, **var)
+        rs = scalar.attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal=causal, **var)
+        np.testing.assert_allclose(r["O"][0, 0], np.array(rs, dtype=float), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_uniform_is_the_mean_of_the_kept_values(causal):
+    q, k, v = _rand_qkv(B=1, H=1, N=20, d=8, sigma=1.3, seed=310)
+    S = (q[0, 0] @ k[0, 0].T) / math.sqrt(8)
+    for W in (0.2, 1.0, 2.5):
+        r = oracle.attn_fwd(q, k, v, causal=causal, kind="uniform", window=W)
+        for i in range(20):
+            vis = [(j <= i) if causal else True for j in range(20)]
+            keep = _support(S[i].tolist(), vis, W)
+            np.testing.assert_allclose(r["O"][0, 0, i], v[0, 0][keep].mean(axis=0), atol=1e-13)
+            assert r["l"][0, 0, i] == len(keep)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_trunc_is_softmax_renormalised_over_the_support(causal):
+    q, k, v = _rand_qkv(B=1, H=1, N=20, d=8, sigma=1.3, seed=320)
+    S = (q[0, 0] @ k[0, 0].T) / math.sqrt(8)
+    mask = np.tril(np.ones((20, 20), bool)) if causal else np.ones((20, 20), bool)
+    P = torch.softmax(torch.from_numpy(np.where(mask, S, -np.inf)), dim=-1).numpy()   # library softmax
+    for W in (0.2, 1.0, 2.5):
+        r = oracle.attn_fwd(q, k, v, causal=causal, kind="trunc", window=W)
+        for i in range(20):
+            keep = _support(S[i].tolist(), mask[i].tolist(), W)
+            p = np.zeros(20)
+            p[keep] = P[i, keep] / P[i, keep].sum()
+            np.testing.assert_allclose(r["O"][0, 0, i], p @ v[0, 0], atol=1e-13)
+
+
+def test_wide_window_trunc_is_exact_softmax_and_uniform_is_the_plain_mean():
+    q, k, v = _rand_qkv(B=1, H=2, N=16, d=8, sigma=1.0, seed=330)
+    S = np.einsum("bhnd,bhmd->bhnm", q, k) / math.sqrt(8)
+    W = float(S.max() - S.min()) + 1.0                       # every visible key is kept
+    r = oracle.attn_fwd(q, k, v, kind="trunc", window=W)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                                           torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(r["O"], ref, atol=1e-12)
+    ru = oracle.attn_fwd(q, k, v, kind="uniform", window=W)
+    np.testing.assert_allclose(ru["O"], np.broadcast_to(v.mean(axis=2, keepdims=True), ru["O"].shape), atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["trunc", "uniform"])
+def test_narrow_window_keeps_only_the_row_maximum(kind):
+    q, k, v = _rand_qkv(B=1, H=1, N=12, d=8, sigma=1.0, seed=340)
+    S = (q[0, 0] @ k[0, 0].T) / math.sqrt(8)
+    top2 = np.sort(S, axis=1)[:, -2:]
+    W = 0.5 * float((top2[:, 1] - top2[:, 0]).min())          # below every row's top gap
+    r = oracle.attn_fwd(q, k, v, kind=kind, window=W)
+    np.testing.assert_allclose(r["O"][0, 0], v[0, 0][S.argmax(axis=1)], atol=1e-15)
+    idx = oracle.attn_fwd(q, k, v, kind=kind, window=W, detail=True)["idx"][0, 0]
+    assert np.all((idx == 0).sum(axis=1) == 1) and np.all((idx == oracle.IDX_FLUSHED).sum(axis=1) == 11)
+
+
+@pytest.mark.parametrize("kind", ["trunc", "uniform"])
+def test_support_edge_is_inclusive(kind):
+    # integer scores with scale 1: the key at exactly m - W is kept, the one just below is not
+    q = np.array([[[[1.0, 0.0]]]])
+    k = np.array([[[[5.0, 0.0], [3.0, 0.0], [2.0, 0.0], [4.0, 0.0]]]])
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0], [7.0, 7.0], [0.0, 0.0]]]])
+    r = oracle.attn_fwd(q, k, v, kind=kind, window=2.0, scale=1.0, detail=True)
+    assert r["idx"][0, 0, 0].tolist() == [0, 0, oracle.IDX_FLUSHED, 0]
+    w = np.array([1.0, math.exp(-2.0), 0.0, math.exp(-1.0)]) if kind == "trunc" else np.array([1.0, 1.0, 0.0, 1.0])
+    np.testing.assert_allclose(r["O"][0, 0, 0], (w @ v[0, 0, :, :]) / w.sum(), atol=1e-15)
