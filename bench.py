@@ -173,7 +173,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_8k", choices=sorted(qin.WORKLOADS))
     ap.add_argument("--dtype", default=None, choices=["fp8", "bf16", "f32"])
-    ap.add_argument("--kind", default="pot", choices=["pot", "exact", "exact_anchored", "kint"])
+    ap.add_argument("--kind", default="pot", choices=["pot", "exact", "exact_anchored", "kint", "trunc", "uniform"])
     ap.add_argument("--levels", type=int, default=16)
     ap.add_argument("--window", type=float, default=None)
     ap.add_argument("--interp", action="store_true")
@@ -211,6 +211,8 @@ def main(argv=None):
         var["levels"] = args.levels
     if args.window is not None:
         var["window"] = args.window
+    elif args.kind in ("trunc", "uniform"):
+        var["window"] = 8.0     # support width W (score units)
     if args.interp:
         var["interp"] = True
     dtn = DT_NAME[x.q.dtype]
@@ -256,7 +258,9 @@ def main(argv=None):
                           ("pot16", {"kind": "pot", "levels": 16}), ("pot8", {"kind": "pot", "levels": 8}),
                           ("kint16_window8_hard", {"kind": "kint", "levels": 16, "window": 8.0}),
                           ("kint16_minmax_hard", {"kind": "kint", "levels": 16}),
-                          ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True})]:
+                          ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True}),
+                          ("trunc_window2", {"kind": "trunc", "window": 2.0}),
+                          ("uniform_window2", {"kind": "uniform", "window": 2.0})]:
             for c in (False, True):
                 t, host = time_calls(lambda: call(dev_t, x, vv, c, out), args.variant_calls)
                 Pc = pairs(B, H, N, c)

@@ -93,6 +93,15 @@ typedef enum {
  *                     the same pre-pass the grid variants use, w = exp(s - m)
  *                     with no running rescale: the grid kernels with the
  *                     exponential put back, for like-for-like timing.
+ * QSA_TRUNC           support truncation: the keys with s >= m - window keep
+ *                     their exact weight exp(s - m), every other key gets 0
+ *                     (the sensitivity study of "Approximating Softmax in
+ *                     Pretrained LLMs", abstract: the support can be cut near
+ *                     the row maximum).
+ * QSA_UNIFORM         uniform weighting of the same support: weight 1 for the
+ *                     keys with s >= m - window, 0 for the others, so each row
+ *                     of O is the mean of the kept rows of V (the same study:
+ *                     equal weights on the kept positions hurt).
  *
  * QSA_F_INTERP        K-interval only: linear interpolation.
  * QSA_F_WINDOW        K-interval only: fixed-window calibration [m - window, m].
@@ -107,6 +116,8 @@ enum {
   QSA_KINT = 1,
   QSA_POT = 2,
   QSA_EXACT_ANCHORED = 3,
+  QSA_TRUNC = 4,
+  QSA_UNIFORM = 5,
   QSA_BASE_MASK = 0x0F,
   QSA_F_INTERP = 1 << 4,
   QSA_F_WINDOW = 1 << 5,
@@ -124,7 +135,8 @@ enum {
  *   QSA_KINT: 1 <= k_levels <= 64;  QSA_POT: 1 <= k_levels <= 64
  *   (fp8: k_levels <= 16, so the power-of-two weights stay exact in the
  *   8-bit operand of the PV product);
- *   QSA_F_WINDOW: window finite and > 0;  flags only on the kinds above.
+ *   QSA_F_WINDOW, QSA_TRUNC, QSA_UNIFORM: window finite and > 0;
+ *   flags only on the kinds above (none on QSA_TRUNC and QSA_UNIFORM).
  */
 
 /*
@@ -139,7 +151,8 @@ enum {
  *   variant   base kind | flags (above).
  *   k_levels  K (K-interval intervals) or L (PoT levels); ignored by the
  *             exact kinds.
- *   window    W for QSA_F_WINDOW, in units of the scaled score; else ignored.
+ *   window    W for QSA_F_WINDOW, QSA_TRUNC and QSA_UNIFORM, in units of the
+ *             scaled score; else ignored.
  *   dtype     a qsa_dtype.
  *   stream    hipStream_t or NULL.
  * scale = 1/sqrt(d); fp8 descales 1.  Returns a qsa_status.
@@ -157,15 +170,19 @@ typedef struct {
   float v_descale;
   float* row_max;              /* [B,H,N] float32: m_i (the anchor).                     */
   float* row_lo;               /* [B,H,N] float32: K-interval: the calibrated lower end  */
-                               /*   lo_i; other anchored kinds: the visible row minimum. */
+                               /*   lo_i; QSA_TRUNC / QSA_UNIFORM: the support edge      */
+                               /*   m_i - window; other anchored kinds: the visible row  */
+                               /*   minimum.                                             */
                                /*   Not available for QSA_EXACT (must be NULL).          */
   float* row_sum;              /* [B,H,N] float32: l_i = sum_j w_ij of the weights that  */
                                /*   entered the PV product (QSA_EXACT: relative to the   */
                                /*   final running maximum).                              */
   unsigned char* grid_idx;     /* [B,H,idx_rows,N] u8: per element the grid index l (K-  */
                                /*   interval; interpolation: floor(y) clipped to K) or   */
-                               /*   the exponent e (PoT); 0 for exact kinds;             */
-                               /*   QSA_IDX_FLUSHED / QSA_IDX_MASKED otherwise.          */
+                               /*   the exponent e (PoT); 0 for exact kinds and for the  */
+                               /*   kept keys of QSA_TRUNC / QSA_UNIFORM;                */
+                               /*   QSA_IDX_FLUSHED (also: outside the support) /        */
+                               /*   QSA_IDX_MASKED otherwise.                            */
   int idx_row0;                /* first query row dumped into grid_idx                   */
   int idx_rows;                /* number of query rows dumped (0: none)                  */
 } qsa_fwd_ex_opts;

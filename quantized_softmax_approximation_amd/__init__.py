@@ -18,13 +18,13 @@ from typing import Optional
 import torch
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_validate", "variant_code", "status_string", "last_error",
-           "version", "lib", "lib_path", "QSAError", "EXACT", "KINT", "POT", "EXACT_ANCHORED", "F_INTERP",
+           "version", "lib", "lib_path", "QSAError", "EXACT", "KINT", "POT", "EXACT_ANCHORED", "TRUNC", "UNIFORM", "F_INTERP",
            "F_WINDOW", "F_FLUSH", "DT_F32", "DT_BF16", "DT_FP8_E4M3", "IDX_FLUSHED", "IDX_MASKED"]
 
 # ABI constants (include/qsa.h)
 OK, ERR_NULL_PTR, ERR_SHAPE, ERR_PARAM, ERR_UNSUPPORTED, ERR_HIP = range(6)
 DT_F32, DT_BF16, DT_FP8_E4M3 = 0, 1, 2
-EXACT, KINT, POT, EXACT_ANCHORED = 0, 1, 2, 3
+EXACT, KINT, POT, EXACT_ANCHORED, TRUNC, UNIFORM = 0, 1, 2, 3, 4, 5
 F_INTERP, F_WINDOW, F_FLUSH = 1 << 4, 1 << 5, 1 << 6
 IDX_FLUSHED, IDX_MASKED = 254, 255
 
@@ -88,8 +88,12 @@ def version() -> int:
 
 def variant_code(kind: str = "exact", *, interp: bool = False, window: Optional[float] = None,
                  flush: bool = False) -> int:
-    """Variant bits for kind in {"exact", "exact_anchored", "kint", "pot"} plus flags."""
-    base = {"exact": EXACT, "kint": KINT, "pot": POT, "exact_anchored": EXACT_ANCHORED}[kind]
+    """Variant bits for kind in {"exact", "exact_anchored", "kint", "pot", "trunc", "uniform"} plus
+    flags.  For "trunc" and "uniform" the window is the support width W, not a flag."""
+    base = {"exact": EXACT, "kint": KINT, "pot": POT, "exact_anchored": EXACT_ANCHORED, "trunc": TRUNC,
+            "uniform": UNIFORM}[kind]
+    if base in (TRUNC, UNIFORM):
+        return base | (F_INTERP if interp else 0) | (F_FLUSH if flush else 0)
     return base | (F_INTERP if interp else 0) | (F_WINDOW if window is not None else 0) | (F_FLUSH if flush else 0)
 
 

@@ -43,7 +43,13 @@ int validate(int B, int H, int Hkv, int N, int d, int causal, int variant, int k
   const int flags = variant & ~QSA_BASE_MASK;
   if (flags & ~(QSA_F_INTERP | QSA_F_WINDOW | QSA_F_FLUSH))
     return fail(QSA_ERR_PARAM, "unknown variant flag bits 0x%x", flags);
-  if (base > QSA_EXACT_ANCHORED) return fail(QSA_ERR_PARAM, "unknown variant kind %d", base);
+  if (base > QSA_UNIFORM) return fail(QSA_ERR_PARAM, "unknown variant kind %d", base);
+  if (base == QSA_TRUNC || base == QSA_UNIFORM) {
+    if (flags) return fail(QSA_ERR_PARAM, "support truncation and uniform weighting take no flags");
+    if (!(std::isfinite(window) && window > 0.0f))
+      return fail(QSA_ERR_PARAM, "support truncation and uniform weighting need a finite window > 0 (got %g)",
+                  (double)window);
+  }
   if (base != QSA_KINT && (flags & (QSA_F_INTERP | QSA_F_WINDOW)))
     return fail(QSA_ERR_PARAM, "interpolation and fixed-window calibration are K-interval options");
   if ((base == QSA_EXACT || base == QSA_EXACT_ANCHORED) && (flags & QSA_F_FLUSH))
@@ -69,6 +75,8 @@ int weight_kind(int variant) {
     case QSA_EXACT: return qsa::WK_EXACT;
     case QSA_EXACT_ANCHORED: return qsa::WK_EXACT_ANCH;
     case QSA_POT: return flush ? qsa::WK_POT_FLUSH : qsa::WK_POT;
+    case QSA_TRUNC: return qsa::WK_TRUNC;
+    case QSA_UNIFORM: return qsa::WK_UNIF;
     default: return interp ? (flush ? qsa::WK_KI_FLUSH : qsa::WK_KI) : (flush ? qsa::WK_KH_FLUSH : qsa::WK_KH);
   }
 }
@@ -124,7 +132,7 @@ int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, int B,
   a.causal = causal ? 1 : 0;
   a.levels = k_levels;
   a.window_calib = (base == QSA_KINT && (variant & QSA_F_WINDOW)) ? 1 : 0;
-  a.window = a.window_calib ? window : 0.0f;
+  a.window = (a.window_calib || base == QSA_TRUNC || base == QSA_UNIFORM) ? window : 0.0f;
   const float scale = x.scale > 0.0f ? x.scale : 1.0f / std::sqrt((float)d);
   const float qd = x.q_descale > 0.0f ? x.q_descale : 1.0f;
   const float kd = x.k_descale > 0.0f ? x.k_descale : 1.0f;

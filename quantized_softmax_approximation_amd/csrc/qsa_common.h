@@ -16,8 +16,14 @@ enum WeightKind : int {
   WK_KH_FLUSH = 5,     // K-interval, hard rounding, below window -> 0
   WK_KI = 6,           // K-interval, linear interpolation
   WK_KI_FLUSH = 7,     // K-interval, interpolation, below window -> 0
-  WK_COUNT = 8
+  WK_TRUNC = 8,        // exp(s - m) on the support s >= m - W, else 0
+  WK_UNIF = 9,         // 1 on the support s >= m - W, else 0
+  WK_COUNT = 10
 };
+
+// K-interval kinds (per-row grid table) and support kinds (truncation, uniform weighting).
+__host__ __device__ constexpr bool wk_kint(int wk) { return wk >= WK_KH && wk <= WK_KI_FLUSH; }
+__host__ __device__ constexpr bool wk_support(int wk) { return wk == WK_TRUNC || wk == WK_UNIF; }
 
 // Everything a launch needs; passed by value as the kernel argument.
 struct FwdArgs {

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
   constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
+  constexpr bool SUPPORT = wk_support(WK), UNIF = (WK == WK_UNIF);
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -250,6 +251,17 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
             const float y0 = ANCH ? x0 * rc.c : fmaf(x0, rc.c, -rc.mc);
             const float y1 = ANCH ? x1 * rc.c : fmaf(x1, rc.c, -rc.mc);
             pk = pack_bf16(__builtin_amdgcn_exp2f(y0), __builtin_amdgcn_exp2f(y1));
+          } else if (SUPPORT) {
+            // truncation / uniform weighting: keys with y = (M - acc) c > W log2 e are outside
+            // the support; inside, exp(s - m) or 1
+            const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
+            const float e0 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x0 * rc.c);
+            const float e1 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x1 * rc.c);
+            pk = pack_bf16(y0 > rc.cut ? 0.0f : e0, y1 > rc.cut ? 0.0f : e1);
+            if (DUMP) {
+              i0 = y0 > rc.cut ? 254u : 0u;
+              i1 = y1 > rc.cut ? 254u : 0u;
+            }
           } else if (POT && !FLUSH) {
             // t = 2^24 + (acc - M) c = 2^24 - y, rounded to an integer by the FMA itself
             const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
@@ -412,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     const size_t ri = (size_t)bh * N + row;
     if (a.row_max) a.row_max[ri] = M * a.sc;
     if (a.row_sum) a.row_sum[ri] = lt;
-    if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
+    if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
   }
 #endif
 }
@@ -446,6 +458,8 @@ hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
     case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
     case WK_KI: return launch_one<D, WK_KI>(a, st);
     case WK_KI_FLUSH: return launch_one<D, WK_KI_FLUSH>(a, st);
+    case WK_TRUNC: return launch_one<D, WK_TRUNC>(a, st);
+    case WK_UNIF: return launch_one<D, WK_UNIF>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
   const size_t ri = (size_t)bh * N + row;
   if (a.row_max) a.row_max[ri] = M * a.sc;
   if (a.row_sum) a.row_sum[ri] = l;
-  if (a.row_lo) a.row_lo[ri] = (WK >= WK_KH && a.window_calib) ? M * a.sc - a.window : MN * a.sc;
+  if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
 }
 
 template <int D, int WK>
@@ -158,6 +158,8 @@ hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
     case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
     case WK_KI: return launch_one<D, WK_KI>(a, st);
     case WK_KI_FLUSH: return launch_one<D, WK_KI_FLUSH>(a, st);
+    case WK_TRUNC: return launch_one<D, WK_TRUNC>(a, st);
+    case WK_UNIF: return launch_one<D, WK_UNIF>(a, st);
   }
   return hipErrorInvalidValue;
 }

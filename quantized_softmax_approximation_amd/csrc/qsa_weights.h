@@ -7,7 +7,7 @@
 //
 //   y = (M - acc) * c     M = row maximum of acc over the visible keys
 //
-// exact / PoT: c = scale * log2(e), so y = (m - s) log2(e);
+// exact / PoT / support kinds: c = scale * log2(e), so y = (m - s) log2(e);
 // K-interval:  c = scale / Delta,   so y = (m - s) / Delta.
 //
 // Rowmax-PoT ("Approximating Softmax in Pretrained LLMs", abstract; the wiki
@@ -19,6 +19,11 @@
 // Attention", abstract and chapter 1): w is read off a table of K+1 grid
 // values T_l = exp(-l Delta) kept per row in LDS; hard rounding takes the
 // nearest grid point, interpolation the straight line between neighbours.
+//
+// Support truncation and uniform weighting (the sensitivity study of
+// "Approximating Softmax in Pretrained LLMs", abstract): keys with
+// s >= m - W keep exp(s - m) or 1, the others get 0; in y units the edge is
+// y = W log2(e) (RowC::cut).
 #pragma once
 
 #include "qsa_common.h"
@@ -35,6 +40,7 @@ struct RowC {
   float c;      // multiplier on (M - acc)
   float mc;     // M * c
   uint32_t tab; // K-interval: byte offset of this row's column in the LDS table
+  float cut;    // support kinds: the support edge W log2(e) in y units
 };
 
 // Table layout (K-interval): entry l of local row r sits at byte
@@ -140,6 +146,21 @@ template <bool FLUSH> struct KInterpW {
 template <> struct Weight<WK_KI> : KInterpW<false> {};
 template <> struct Weight<WK_KI_FLUSH> : KInterpW<true> {};
 
+// Support truncation (UNIF = false) and uniform weighting (UNIF = true).
+template <bool UNIF> struct SupportW {
+  template <int SH>
+  static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char*, int) {
+    const float y = fmaf(acc, -r.c, r.mc);
+    if (y > r.cut) return 0.0f;
+    return UNIF ? 1.0f : __builtin_amdgcn_exp2f(-y);
+  }
+  static __device__ __forceinline__ uint32_t idx(float acc, const RowC& r, int) {
+    return fmaf(acc, -r.c, r.mc) > r.cut ? 254u : 0u;
+  }
+};
+template <> struct Weight<WK_TRUNC> : SupportW<false> {};
+template <> struct Weight<WK_UNIF> : SupportW<true> {};
+
 // Per-row constants from the pre-pass extrema (raw units) and, for
 // K-interval, the row's grid table written into LDS.  The K+1 table entries
 // are split between the `nsplit` lanes that share a row (this lane writes
@@ -149,7 +170,8 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
                                          unsigned char* tab, int part, int nsplit) {
   RowC rc;
   rc.tab = 0;
-  if (WK < WK_KH) {
+  rc.cut = a.window * kLog2e;
+  if (!wk_kint(WK)) {
     rc.c = a.sc * kLog2e;
     rc.mc = M * rc.c;
     return rc;

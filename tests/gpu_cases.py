@@ -29,8 +29,11 @@ KI4W = dict(kind="kint", levels=4, window=8.0, interp=True)
 KI16W = dict(kind="kint", levels=16, window=8.0, interp=True)
 KH4WF = dict(kind="kint", levels=4, window=3.0, flush=True)
 KI4WF = dict(kind="kint", levels=4, window=3.0, interp=True, flush=True)
+TRUNC2 = dict(kind="trunc", window=2.0)
+UNIF2 = dict(kind="uniform", window=2.0)
 
-ALL = [EXACT, EXACT_ANCH, POT8, POT16, POT4F, KH4, KH16, KI4, KI16, KH4W, KH16W, KI4W, KI16W, KH4WF, KI4WF]
+ALL = [EXACT, EXACT_ANCH, POT8, POT16, POT4F, KH4, KH16, KI4, KI16, KH4W, KH16W, KI4W, KI16W, KH4WF, KI4WF,
+       TRUNC2, UNIF2]
 
 
 def name(var):

@@ -48,7 +48,8 @@ def test_version_and_status_strings():
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name, val in [("QSA_EXACT", qsa.EXACT), ("QSA_KINT", qsa.KINT), ("QSA_POT", qsa.POT),
-                      ("QSA_EXACT_ANCHORED", qsa.EXACT_ANCHORED), ("QSA_DT_F32", qsa.DT_F32),
+                      ("QSA_EXACT_ANCHORED", qsa.EXACT_ANCHORED), ("QSA_TRUNC", qsa.TRUNC),
+                      ("QSA_UNIFORM", qsa.UNIFORM), ("QSA_DT_F32", qsa.DT_F32),
                       ("QSA_DT_BF16", qsa.DT_BF16), ("QSA_DT_FP8_E4M3", qsa.DT_FP8_E4M3)]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
@@ -63,7 +64,8 @@ def test_valid_arguments():
     for var, kl, w in [(qsa.EXACT, 0, 0.0), (qsa.EXACT_ANCHORED, 0, 0.0), (qsa.KINT, 4, 0.0),
                        (qsa.KINT | qsa.F_INTERP, 16, 0.0), (qsa.KINT | qsa.F_WINDOW, 16, 8.0),
                        (qsa.KINT | qsa.F_WINDOW | qsa.F_FLUSH | qsa.F_INTERP, 64, 8.0),
-                       (qsa.POT | qsa.F_FLUSH, 64, 0.0), (qsa.POT, 1, 0.0)]:
+                       (qsa.POT | qsa.F_FLUSH, 64, 0.0), (qsa.POT, 1, 0.0), (qsa.TRUNC, 0, 2.0),
+                       (qsa.UNIFORM, 0, 0.5)]:
         assert v(variant=var, k_levels=kl, window=w) == qsa.OK, (var, kl, w)
     assert v(d=128, N=1, H=64, Hkv=8) == qsa.OK
     assert v(dtype=qsa.DT_F32) == qsa.OK
@@ -75,7 +77,11 @@ def test_valid_arguments():
     (dict(d=96), qsa.ERR_UNSUPPORTED), (dict(d=256), qsa.ERR_UNSUPPORTED),
     (dict(B=1024, H=64, N=65536, d=128), qsa.ERR_SHAPE),
     (dict(dtype=3), qsa.ERR_PARAM), (dict(dtype=-1), qsa.ERR_PARAM),
-    (dict(variant=4), qsa.ERR_PARAM), (dict(variant=qsa.POT | (1 << 8)), qsa.ERR_PARAM),
+    (dict(variant=6), qsa.ERR_PARAM), (dict(variant=qsa.POT | (1 << 8)), qsa.ERR_PARAM),
+    (dict(variant=qsa.TRUNC, window=0.0), qsa.ERR_PARAM), (dict(variant=qsa.UNIFORM, window=-2.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.TRUNC, window=math.inf), qsa.ERR_PARAM), (dict(variant=qsa.UNIFORM, window=math.nan), qsa.ERR_PARAM),
+    (dict(variant=qsa.TRUNC | qsa.F_FLUSH, window=2.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.UNIFORM | qsa.F_WINDOW, window=2.0), qsa.ERR_PARAM),
     (dict(variant=qsa.POT | qsa.F_INTERP), qsa.ERR_PARAM), (dict(variant=qsa.POT | qsa.F_WINDOW, window=8.0), qsa.ERR_PARAM),
     (dict(variant=qsa.EXACT | qsa.F_FLUSH), qsa.ERR_PARAM),
     (dict(variant=qsa.EXACT_ANCHORED | qsa.F_FLUSH), qsa.ERR_PARAM),

@@ -27,7 +27,8 @@ def _gpu():
 
 # ---------------------------------------------------------------- tiny (fp32)
 
-TINY_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.KH4, gc.POT8, gc.POT4F, gc.KI4, gc.KH4W, gc.KI4W, gc.KH4WF, gc.KI4WF]
+TINY_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.KH4, gc.POT8, gc.POT4F, gc.KI4, gc.KH4W, gc.KI4W, gc.KH4WF, gc.KI4WF,
+             gc.TRUNC2, gc.UNIF2]
 
 
 @pytest.mark.parametrize("var", TINY_VARS, ids=gc.name)
@@ -37,7 +38,8 @@ def test_tiny_fp32(var):
 
 # ---------------------------------------------------------------- GPT-2 shaped (bf16, causal)
 
-GPT2_VARS = [gc.EXACT, gc.POT8, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KH16W, gc.KI4W, gc.KI16W]
+GPT2_VARS = [gc.EXACT, gc.POT8, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KH16W, gc.KI4W, gc.KI16W, gc.TRUNC2,
+             gc.UNIF2]
 
 
 @pytest.fixture(scope="module")
@@ -79,7 +81,7 @@ def gqa16k():
 
 
 @pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT16, gc.KH4, gc.KH16, gc.KI16, gc.KH4W,
-                                 gc.KH16W, gc.KI4W], ids=gc.name)
+                                 gc.KH16W, gc.KI4W, gc.TRUNC2, gc.UNIF2], ids=gc.name)
 def test_gqa16k_sampled(gqa16k, var):
     wl, x, dev_t, f64 = gqa16k
     heads = [(0, 0), (0, 9), (0, 63)]
@@ -98,7 +100,7 @@ def test_ragged(N, d, causal):
     wl = qin.custom(f"ragged{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype="bf16", causal=causal, sigma_qk=1.5, seed=N + d)
     x = qin.make_inputs(wl)
     dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
-    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF):
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2, gc.UNIF2):
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
 
 
@@ -106,7 +108,7 @@ def test_ragged(N, d, causal):
 def test_ragged_fp32(N):
     wl = qin.custom(f"f32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
     x = qin.make_inputs(wl)
-    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W):
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W, gc.TRUNC2, gc.UNIF2):
         gc.run_parity(wl, var, x=x, verbose=False)
 
 
@@ -160,7 +162,7 @@ def test_row_stats_match_oracle():
     x = qin.make_inputs(wl)
     dev_t = gc.to_gpu(x)
     qf, kf, vf = gc.decoded(x)
-    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KH4W, gc.EXACT_ANCH):
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KH4W, gc.EXACT_ANCH, gc.TRUNC2, gc.UNIF2):
         o, _, st = gc.gpu_call(x, dev_t, var, causal=True, stats=True)
         for h in range(2):
             ref = oracle.head_rows(qf[0, h], kf[0, h], vf[0, h], causal=True, **gc.oracle_var(var))
@@ -173,6 +175,19 @@ def test_row_stats_match_oracle():
             if var["kind"] != "exact":
                 lo = st["row_lo"][0, h].cpu().numpy()
                 assert np.all(np.abs(lo - ref["lo"]) <= dstar + 1e-5 * (1 + np.abs(ref["lo"])))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_support_window_extremes(dtype):
+    # a window far below the top score gap keeps only the row maximum; one wider than every
+    # score range keeps every visible key (truncation = exact softmax, uniform = mean of V)
+    d = 128 if dtype != "f32" else 64
+    wl = qin.custom(f"support_{dtype}", B=1, H=2, N=150, d=d, dtype=dtype, causal=True, sigma_qk=1.5, seed=21)
+    x = qin.make_inputs(wl)
+    dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+    for var in (dict(kind="trunc", window=1e-3), dict(kind="uniform", window=1e-3), dict(kind="trunc", window=1e4),
+                dict(kind="uniform", window=1e4)):
+        gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
 
 
 def test_deterministic_and_gqa_equals_repeated_kv():
@@ -228,7 +243,8 @@ def fp8_8k():
     return wl, x, gc.to_gpu(x), gc.decoded(x)
 
 
-FP8_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT8, gc.POT4F, gc.KH16W, gc.KH16, gc.KI16W, gc.KH4WF]
+FP8_VARS = [gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT8, gc.POT4F, gc.KH16W, gc.KH16, gc.KI16W, gc.KH4WF, gc.TRUNC2,
+            gc.UNIF2]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -246,5 +262,6 @@ def test_fp8_ragged(N, d, causal):
     wl = qin.custom(f"fp8_{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype="fp8", causal=causal, sigma_qk=1.5, seed=3 * N + d)
     x = qin.make_inputs(wl)
     dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
-    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF):
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2,
+                gc.UNIF2):
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
