@@ -149,6 +149,109 @@ def cpu_baseline(x, var, causal, budget_s):
                       f"{el:.1f} s, float64 NumPy; rate scaled to credited TFLOP/s (4 d flops per visible pair)"}
 
 
+def board_energy(fn, seconds):
+    """Board energy per call of fn during back-to-back calls, from the GPU's energy accumulator
+    read through amdsmi (the one GPU of the process).  A side thread reads the accumulator twice
+    while the queued calls keep the GPU busy; the mean board power is the energy difference over
+    the difference of the counter's own timestamps (it updates on its own schedule), and the
+    energy per call is that power times the call's HIP-event time.  Returns a dict, or one with
+    an "error" entry when the counter cannot be read."""
+    import threading
+    try:
+        import amdsmi
+    except ImportError as e:
+        return {"error": f"amdsmi not importable: {e}"}
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as e:      # the library raises its own exception types
+        return {"error": f"amdsmi_init failed: {e}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return {"error": f"expected one GPU, amdsmi lists {len(handles)}"}
+        h = handles[0]
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):                        # size the run on completed calls
+            fn()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 3
+        lead = 0.3
+        calls = max(10, min(200000, int(math.ceil((seconds + 2 * lead) / per))))
+        rd = {}
+
+        def reader():
+            time.sleep(lead)
+            rd["e0"] = amdsmi.amdsmi_get_energy_count(h)
+            time.sleep(seconds)
+            rd["e1"] = amdsmi.amdsmi_get_energy_count(h)
+            rd["t1"] = time.perf_counter()
+
+        e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        th = threading.Thread(target=reader)
+        e_start.record()
+        th.start()
+        for _ in range(calls):
+            fn()
+        e_end.record()
+        torch.cuda.synchronize()
+        t_done = time.perf_counter()
+        th.join()
+        ms = e_start.elapsed_time(e_end) / calls
+        e0, e1 = rd["e0"], rd["e1"]
+        joules = (e1["energy_accumulator"] - e0["energy_accumulator"]) * e0["counter_resolution"] * 1e-6
+        dt = (e1["timestamp"] - e0["timestamp"]) * 1e-9
+        watts = joules / dt if dt > 0 else float("nan")
+        return {"joules_per_call": watts * ms * 1e-3, "mean_watts": watts, "ms_per_call": ms, "calls": calls,
+                "counter_seconds": dt, "readings_inside_busy_window": rd["t1"] < t_done,
+                "counter_resolution_uJ": e0["counter_resolution"]}
+    except Exception as e:
+        return {"error": f"energy counter: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def energy_run(args):
+    """Board energy per forward, Rowmax-PoT against the same kernel with exact exp and the online
+    control, on the causal 16K GQA workload (B 1, H 64, Hkv 8, N 16384, d 128, bf16) and on the
+    causal fp8 8K workload.  Board power drifts as the card warms, so the kinds alternate over
+    `--energy-rounds` rounds and the means are reported."""
+    kinds = (("pot16", {"kind": "pot", "levels": 16}), ("exact_anchored", {"kind": "exact_anchored"}),
+             ("exact_online", {"kind": "exact"}))
+    rec = {"metric": "board energy per attention forward (J), amdsmi energy accumulator",
+           "seconds_per_measurement": args.energy_seconds, "rounds": args.energy_rounds, "workloads": {}}
+    for wname in ("gqa16k", "fp8_8k"):
+        wl = qin.WORKLOADS[wname].replace(causal=True)
+        x = qin.make_inputs(wl)
+        dev_t = tuple(t.cuda() for t in (x.q, x.k, x.v))
+        B, H, N, d = x.q.shape
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        runs = {name: [] for name, _ in kinds}
+        print(f"[energy] {wname} warm-up", file=sys.stderr, flush=True)
+        board_energy(lambda: call(dev_t, x, kinds[0][1], True, out), args.energy_seconds)   # card to load power
+        for r in range(args.energy_rounds):
+            for name, var in kinds:
+                print(f"[energy] {wname} round {r} {name}", file=sys.stderr, flush=True)
+                runs[name].append(board_energy(lambda: call(dev_t, x, var, True, out), args.energy_seconds))
+        w = {"config": {"B": B, "H": H, "Hkv": x.k.shape[1], "N": N, "d": d, "causal": True,
+                        "dtype": DT_NAME[x.q.dtype]}, "runs": runs}
+        if all("joules_per_call" in m for ms in runs.values() for m in ms):
+            mean = {n: float(np.mean([m["joules_per_call"] for m in ms])) for n, ms in runs.items()}
+            w["joules_per_call"] = mean
+            w["ms_per_call"] = {n: float(np.mean([m["ms_per_call"] for m in ms])) for n, ms in runs.items()}
+            w["pot_energy_vs_exact_anchored"] = mean["pot16"] / mean["exact_anchored"]
+            w["pot_energy_vs_exact_online"] = mean["pot16"] / mean["exact_online"]
+        rec["workloads"][wname] = w
+        del x, dev_t, out
+        torch.cuda.empty_cache()
+    print(json.dumps(rec))
+    return 0
+
+
 def traffic_for(workload, dtype, var, causal, per_launch_flops):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources."""
@@ -183,6 +286,11 @@ def main(argv=None):
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--variant-calls", type=int, default=100)
     ap.add_argument("--only-kernel", action="store_true", help="just the timed loop (for profilers)")
+    ap.add_argument("--energy", action="store_true",
+                    help="instead of the throughput line: board energy per forward on the causal 16K GQA "
+                         "workload, PoT against the exact kinds (amdsmi energy counter)")
+    ap.add_argument("--energy-seconds", type=float, default=2.0)
+    ap.add_argument("--energy-rounds", type=int, default=2)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernel: also run a plain device copy of this many bytes `steps` times "
                          "(the known-size reference for HBM traffic counters)")
@@ -196,6 +304,8 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
+    if args.energy:
+        return energy_run(args)
     wl = qin.WORKLOADS[args.workload]
     if args.dtype:
         wl = wl.replace(dtype=args.dtype)
