@@ -130,13 +130,16 @@ def _check_kind(kind, levels, window, interp, flush):
 
 
 def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Optional[int] = None,
-                window: Optional[float] = None, interp: bool = False, flush: bool = False):
+                window: Optional[float] = None, interp: bool = False, flush: bool = False,
+                extrema: Optional[tuple] = None):
     """Weights for a block of score rows.
 
     S: (R, N) float64 scaled scores; visible: (R, N) bool, at least one True
     per row.  Returns dict with w (R,N), idx (R,N) uint8, y (R,N) grid
     coordinate (nan where masked; for exact kinds y = m - s), m, lo, delta (R,)
-    and the table T (R, K+1) for kint.
+    and the table T (R, K+1) for kint.  ``extrema`` = (m, mn), each (R,),
+    replaces the row maximum and minimum (the forward with the calibration held
+    fixed, whose derivative is the detached gradient).
     """
     _check_kind(kind, levels, window, interp, flush)
     R, N = S.shape
@@ -144,6 +147,9 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
     pos = np.where(visible, S, np.inf)
     m = neg.max(axis=1)                                   # row max over visible keys (anchor)
     mn = pos.min(axis=1)                                  # row min over visible keys
+    if extrema is not None:
+        m = np.asarray(extrema[0], dtype=np.float64)
+        mn = np.asarray(extrema[1], dtype=np.float64)
     out = {"m": m}
     idx = np.full((R, N), IDX_MASKED, dtype=np.uint8)
 
@@ -230,7 +236,8 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
 def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Sequence[int]] = None, *,
               causal: bool = False, kind: str = "exact", levels: Optional[int] = None,
               window: Optional[float] = None, interp: bool = False, flush: bool = False,
-              scale: Optional[float] = None, detail: bool = False, chunk: int = 512):
+              scale: Optional[float] = None, detail: bool = False, chunk: int = 512,
+              extrema: Optional[tuple] = None):
     """One (batch, head) pair: qh (N, d), kh/vh (N, d) float64.
 
     ``rows`` selects query rows (default: all).  Returns dict with O (R, d),
@@ -246,7 +253,9 @@ def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Seq
         S = sc * (qh[r] @ kh.T)                            # scaled scores, float64
         cols = np.arange(N)
         visible = (cols[None, :] <= r[:, None]) if causal else np.ones((len(r), N), dtype=bool)
-        rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush)
+        ext = None if extrema is None else (np.asarray(extrema[0])[r], np.asarray(extrema[1])[r])
+        rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush,
+                         extrema=ext)
         w = rw["w"]
         l = w.sum(axis=1)                                  # row sum of the approximate weights
         O = (w @ vh) / l[:, None]                          # normalise, then P.V
@@ -282,3 +291,143 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = Fals
             for key, val in r.items():
                 res.setdefault(key, []).append(val)
     return {key: np.stack(val).reshape((B, H) + val[0].shape) for key, val in res.items()}
+
+
+# ---------------------------------------------------------------------------
+# Attention backward (gradients of sum(dO * O) with respect to q, k, v)
+# ---------------------------------------------------------------------------
+#
+# The pages train with K-interval attention through a surrogate gradient placed
+# before normalisation ("Pretraining Transformers with Quantized Softmax in
+# Attention", abstract) but print no formulas, so the gradient modes here are
+# readings (listed in the design notes):
+#
+# * ``ste``  -- straight-through: the weight's derivative in its own score is
+#   taken to be the weight itself, dw/ds := w, as for exp(s - m).  Then
+#   dS_ij = P_ij (dP_ij - D_i) with P = w / l, dP = dO V^T, D_i = dO_i . O_i.
+#   Placing the surrogate before or after the normalisation gives the same
+#   formula, and the extrema drop out (the m-terms sum to zero), so the mode
+#   has no attached/detached distinction.
+# * ``exact`` -- the derivative of the forward function wherever it exists
+#   (almost everywhere): through each score directly (interpolation: the slope
+#   of the grid line; hard rounding, PoT, uniform: zero) and through the
+#   calibration, i.e. the row maximum m (via y and, for min-max grids, Delta)
+#   and the row minimum lo (min-max grids, via Delta and the grid values
+#   T_l = exp(-l Delta)); those two gradients land on the arg-max and arg-min
+#   keys of the row.
+# * ``exact_detached`` -- the same with m and lo held constant.
+
+def _weight_partials(rw, kind, levels, interp, flush, visible):
+    """dw/dy and dw/dDelta (at fixed y) of each element; y as in row_weights."""
+    R, N = visible.shape
+    z = np.zeros((R, N))
+    if kind != "kint":
+        return z, z
+    K = levels
+    delta = rw["delta"]
+    T = rw["T"]
+    y = np.where(visible, rw["y"], 0.0)
+    rows = np.arange(R)[:, None]
+    ell = np.arange(K + 1, dtype=np.float64)
+    if interp:
+        yc = np.minimum(y, float(K))
+        l0 = np.minimum(np.floor(yc), K - 1).astype(np.int64)
+        t = yc - l0
+        inside = y < K
+        dwdy = np.where(inside, T[rows, l0 + 1] - T[rows, l0], 0.0)
+        dT0 = -l0 * T[rows, l0]                        # dT_l/dDelta = -l T_l
+        dT1 = -(l0 + 1) * T[rows, l0 + 1]
+        dwdD = (1.0 - t) * dT0 + t * dT1
+        beyond = -K * T[:, K:K + 1] * np.ones((1, N))
+        dwdD = np.where(inside, dwdD, 0.0 if flush else beyond)
+    else:
+        l = np.minimum(np.rint(y), K).astype(np.int64)
+        dwdy = np.zeros((R, N))
+        dwdD = -l * T[rows, l]
+        if flush:
+            dwdD = np.where(y <= K, dwdD, 0.0)
+    keep = visible & (delta > 0)[:, None]
+    return np.where(keep, dwdy, 0.0), np.where(keep, dwdD, 0.0)
+
+
+def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window=None, interp=False,
+             flush=False, scale=None, grad="ste", extrema=None):
+    """Gradients for one (batch, head): qh (N, d), kh/vh (N, d), doh (N, d) float64.
+    Returns dict dQ (N, d), dK (N, d), dV (N, d) (this head's share of dK, dV).
+    ``extrema`` (detached mode only) = (m, mn) per row, as in row_weights."""
+    if extrema is not None and grad != "exact_detached":
+        raise ValueError("fixed extrema go with the detached gradient")
+    if grad not in ("ste", "exact", "exact_detached"):
+        raise ValueError(f"unknown gradient mode {grad!r}")
+    N, d = qh.shape
+    sc = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    S = sc * (qh @ kh.T)
+    cols = np.arange(N)
+    visible = (cols[None, :] <= cols[:, None]) if causal else np.ones((N, N), dtype=bool)
+    rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush,
+                     extrema=extrema)
+    w = rw["w"]
+    l = w.sum(axis=1)
+    P = w / l[:, None]
+    O = P @ vh
+    D = (doh * O).sum(axis=1)                               # D_i = dO_i . O_i
+    dP = doh @ vh.T
+    dV = P.T @ doh
+    if grad == "ste":
+        dS = np.where(visible, P * (dP - D[:, None]), 0.0)
+    else:
+        dw = np.where(visible, (dP - D[:, None]) / l[:, None], 0.0)
+        m = rw["m"]
+        if kind == "exact" or kind == "trunc":              # w = exp(s - m) where kept
+            dS = dw * w
+            dm = -(dw * w).sum(axis=1)
+            dlo = np.zeros(N)
+        elif kind == "kint":
+            dwdy, dwdD = _weight_partials(rw, kind, levels, interp, flush, visible)
+            delta = rw["delta"]
+            safe = np.where(delta > 0, delta, 1.0)[:, None]
+            y = np.where(visible, rw["y"], 0.0)
+            dS = dw * dwdy * (-1.0 / safe)                   # y = (m - s) / Delta
+            dm = (dw * dwdy / safe).sum(axis=1)
+            dD = (dw * (dwdD - dwdy * y / safe)).sum(axis=1)  # total dDelta, y moving with Delta
+            if window is None:                                # min-max: Delta = (m - lo) / K
+                dm = dm + dD / levels
+                dlo = -dD / levels
+            else:                                            # window: Delta = W / K is constant
+                dlo = np.zeros(N)
+        else:                                                # pot, uniform: piecewise constant
+            dS = np.zeros((N, N))
+            dm = np.zeros(N)
+            dlo = np.zeros(N)
+        if grad == "exact":
+            rows = np.arange(N)
+            amax = np.argmax(np.where(visible, S, -np.inf), axis=1)
+            amin = np.argmin(np.where(visible, S, np.inf), axis=1)
+            dS = dS.copy()
+            np.add.at(dS, (rows, amax), dm)
+            if kind == "kint" and window is None:
+                np.add.at(dS, (rows, amin), dlo)
+    dQ = sc * (dS @ kh)
+    dK = sc * (dS.T @ qh)
+    return {"dQ": dQ, "dK": dK, "dV": dV}
+
+
+def attn_bwd(q, k, v, do, *, causal=False, kind="exact", levels=None, window=None, interp=False, flush=False,
+             scale=None, grad="ste"):
+    """Attention backward over all heads: q, do (B, H, N, d); k, v (B, Hkv, N, d) float64.
+    dK and dV of a KV head sum the shares of the query heads that read it."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    group = H // Hkv
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            kv = h // group
+            r = head_bwd(q[b, h], k[b, kv], v[b, kv], do[b, h], causal=causal, kind=kind, levels=levels,
+                         window=window, interp=interp, flush=flush, scale=scale, grad=grad)
+            dQ[b, h] = r["dQ"]
+            dK[b, kv] += r["dK"]
+            dV[b, kv] += r["dV"]
+    return {"dQ": dQ, "dK": dK, "dV": dV}

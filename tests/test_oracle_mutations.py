@@ -38,7 +38,8 @@ MUTATIONS = {
     "causal_off_by_one": ("(cols[None, :] <= r[:, None])", "(cols[None, :] <= r[:, None] + 1)"),
     "no_normalisation": ("O = (w @ vh) / l[:, None]", "O = (w @ vh)"),
     "missing_scale": ("S = sc * (qh[r] @ kh.T)", "S = (qh[r] @ kh.T)"),
-    "gqa_wrong_head": ("kv = h // group", "kv = h % Hkv"),
+    "gqa_wrong_head": ("kv = h // group                                # query head h reads",
+                       "kv = h % Hkv                                # query head h reads"),
     "flush_threshold": ("kept = visible & (e <= L - 1)", "kept = visible & (e <= L)"),
     "support_edge_exclusive": ("kept = visible & (m[:, None] - S <= window)", "kept = visible & (m[:, None] - S < window)"),
     "support_sign": ("kept = visible & (m[:, None] - S <= window)", "kept = visible & (S - m[:, None] <= window)"),
