@@ -202,6 +202,9 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
     y = np.where(degenerate[:, None] & visible, 0.0, y)
     yv = np.where(visible, y, 0.0)
     rows = np.arange(R)[:, None]
+    # A min-max grid spans every visible score (y <= K), so flushing removes nothing
+    # there; it applies to fixed-window grids, whose window can end above the row minimum.
+    flush = flush and window is not None
     if not interp:
         l = np.rint(yv)                                   # nearest grid point, half to even
         if flush:
@@ -297,43 +300,61 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = Fals
 # Attention backward (gradients of sum(dO * O) with respect to q, k, v)
 # ---------------------------------------------------------------------------
 #
-# The pages train with K-interval attention through a surrogate gradient placed
-# before normalisation ("Pretraining Transformers with Quantized Softmax in
-# Attention", abstract) but print no formulas, so the gradient modes here are
-# readings (listed in the design notes):
+# The pages train K-interval attention with a straight-through surrogate whose
+# placement relative to the normalisation they vary, with backward rules that
+# include the derivatives through the calibration and with the row extrema
+# either attached or detached ("Pretraining Transformers with Quantized Softmax
+# in Attention", abstract; chapter 5 "Build the method").  They print no
+# formulas, so the gradient modes here are readings (listed in the design notes):
 #
-# * ``ste``  -- straight-through: the weight's derivative in its own score is
-#   taken to be the weight itself, dw/ds := w, as for exp(s - m).  Then
-#   dS_ij = P_ij (dP_ij - D_i) with P = w / l, dP = dO V^T, D_i = dO_i . O_i.
-#   Placing the surrogate before or after the normalisation gives the same
-#   formula, and the extrema drop out (the m-terms sum to zero), so the mode
-#   has no attached/detached distinction.
+# * ``ste_post`` -- surrogate after the normalisation: the normalised weights
+#   P = w / l are passed back as if they were a softmax of the scores, so
+#   dS_ij = P_ij (dP_ij - D_i) with dP = dO V^T and D_i = dO_i . O_i.  The
+#   extrema do not enter, so there is no attached/detached distinction.
+# * ``ste_pre`` -- surrogate before the normalisation, where the forward needs
+#   one: the rounding of the grid coordinate (K-interval hard rounding:
+#   l = rint(y); PoT: e = rint(y)) is passed straight through (dl/dy := 1 where
+#   the clip to the last level is not active, 0 where it is).  Everything else
+#   takes its exact derivative: the normalisation, the interpolation, and the
+#   calibration (the row maximum m through y and, for min-max grids, through
+#   Delta = (m - lo) / K, which also moves the grid values T_l = exp(-l Delta);
+#   the row minimum lo through Delta).  For hard rounding this gives
+#   dw/ds = w inside the clip and dw/dDelta = w (y - l), a calibration term
+#   that the post-normalisation placement does not have.  The gradients of m
+#   and lo land on the arg-max and arg-min keys of the row (first in key order).
 # * ``exact`` -- the derivative of the forward function wherever it exists
-#   (almost everywhere): through each score directly (interpolation: the slope
-#   of the grid line; hard rounding, PoT, uniform: zero) and through the
-#   calibration, i.e. the row maximum m (via y and, for min-max grids, Delta)
-#   and the row minimum lo (min-max grids, via Delta and the grid values
-#   T_l = exp(-l Delta)); those two gradients land on the arg-max and arg-min
-#   keys of the row.
-# * ``exact_detached`` -- the same with m and lo held constant.
+#   (almost everywhere): as ``ste_pre`` but with no surrogate, so hard rounding,
+#   PoT and uniform weights are constant in each score.
+# * ``ste_pre_detached``, ``exact_detached`` -- the same with m and lo held
+#   constant.
+#
+# Rows whose min-max grid has zero width (every visible score equal) get no
+# gradient through their weights in the modes that differentiate the grid.
 
-def _weight_partials(rw, kind, levels, interp, flush, visible):
-    """dw/dy and dw/dDelta (at fixed y) of each element; y as in row_weights."""
+GRADS = ("ste_post", "ste_pre", "ste_pre_detached", "exact", "exact_detached")
+
+
+def _weight_partials(rw, kind, levels, interp, flush, visible, window, ste=False):
+    """dw/dy and dw/dDelta (at fixed y) of each K-interval element; y as in
+    row_weights.  ``ste``: hard rounding passed straight through (dl/dy := 1).
+    At y = K the last interval's slope applies (the side of the visible scores);
+    on a min-max grid every visible key counts as inside (y <= K by construction:
+    the arg-min key sits on y = K whichever way the division rounds)."""
     R, N = visible.shape
     z = np.zeros((R, N))
     if kind != "kint":
         return z, z
     K = levels
+    flush = flush and window is not None
     delta = rw["delta"]
     T = rw["T"]
     y = np.where(visible, rw["y"], 0.0)
     rows = np.arange(R)[:, None]
-    ell = np.arange(K + 1, dtype=np.float64)
     if interp:
         yc = np.minimum(y, float(K))
         l0 = np.minimum(np.floor(yc), K - 1).astype(np.int64)
         t = yc - l0
-        inside = y < K
+        inside = visible if window is None else (y <= K)
         dwdy = np.where(inside, T[rows, l0 + 1] - T[rows, l0], 0.0)
         dT0 = -l0 * T[rows, l0]                        # dT_l/dDelta = -l T_l
         dT1 = -(l0 + 1) * T[rows, l0 + 1]
@@ -341,8 +362,11 @@ def _weight_partials(rw, kind, levels, interp, flush, visible):
         beyond = -K * T[:, K:K + 1] * np.ones((1, N))
         dwdD = np.where(inside, dwdD, 0.0 if flush else beyond)
     else:
-        l = np.minimum(np.rint(y), K).astype(np.int64)
-        dwdy = np.zeros((R, N))
+        r = np.rint(y)
+        l = np.minimum(r, K).astype(np.int64)
+        w = rw["w"]
+        # T_l = exp(-l Delta): with l := y the weight moves as -Delta w in y (zero once clipped)
+        dwdy = np.where(r <= K, -delta[:, None] * w, 0.0) if ste else np.zeros((R, N))
         dwdD = -l * T[rows, l]
         if flush:
             dwdD = np.where(y <= K, dwdD, 0.0)
@@ -351,14 +375,16 @@ def _weight_partials(rw, kind, levels, interp, flush, visible):
 
 
 def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window=None, interp=False,
-             flush=False, scale=None, grad="ste", extrema=None):
+             flush=False, scale=None, grad="ste_post", extrema=None):
     """Gradients for one (batch, head): qh (N, d), kh/vh (N, d), doh (N, d) float64.
     Returns dict dQ (N, d), dK (N, d), dV (N, d) (this head's share of dK, dV).
-    ``extrema`` (detached mode only) = (m, mn) per row, as in row_weights."""
-    if extrema is not None and grad != "exact_detached":
-        raise ValueError("fixed extrema go with the detached gradient")
-    if grad not in ("ste", "exact", "exact_detached"):
+    ``extrema`` (detached modes only) = (m, mn) per row, as in row_weights."""
+    if grad not in GRADS:
         raise ValueError(f"unknown gradient mode {grad!r}")
+    detached = grad.endswith("_detached")
+    if extrema is not None and not detached:
+        raise ValueError("fixed extrema go with a detached gradient")
+    ste = grad.startswith("ste_pre")
     N, d = qh.shape
     sc = (1.0 / math.sqrt(d)) if scale is None else float(scale)
     S = sc * (qh @ kh.T)
@@ -373,7 +399,7 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
     D = (doh * O).sum(axis=1)                               # D_i = dO_i . O_i
     dP = doh @ vh.T
     dV = P.T @ doh
-    if grad == "ste":
+    if grad == "ste_post":
         dS = np.where(visible, P * (dP - D[:, None]), 0.0)
     else:
         dw = np.where(visible, (dP - D[:, None]) / l[:, None], 0.0)
@@ -383,7 +409,7 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
             dm = -(dw * w).sum(axis=1)
             dlo = np.zeros(N)
         elif kind == "kint":
-            dwdy, dwdD = _weight_partials(rw, kind, levels, interp, flush, visible)
+            dwdy, dwdD = _weight_partials(rw, kind, levels, interp, flush, visible, window, ste=ste)
             delta = rw["delta"]
             safe = np.where(delta > 0, delta, 1.0)[:, None]
             y = np.where(visible, rw["y"], 0.0)
@@ -395,11 +421,17 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
                 dlo = -dD / levels
             else:                                            # window: Delta = W / K is constant
                 dlo = np.zeros(N)
+        elif kind == "pot" and ste:                          # 2^-e with e := y = (m - s) log2(e)
+            e = np.rint(np.where(visible, rw["y"], 0.0))
+            g = np.where(visible & (e <= levels - 1), dw * w, 0.0)   # dw/ds = w inside the clip
+            dS = g
+            dm = -g.sum(axis=1)
+            dlo = np.zeros(N)
         else:                                                # pot, uniform: piecewise constant
             dS = np.zeros((N, N))
             dm = np.zeros(N)
             dlo = np.zeros(N)
-        if grad == "exact":
+        if not detached:
             rows = np.arange(N)
             amax = np.argmax(np.where(visible, S, -np.inf), axis=1)
             amin = np.argmin(np.where(visible, S, np.inf), axis=1)
@@ -413,7 +445,7 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
 
 
 def attn_bwd(q, k, v, do, *, causal=False, kind="exact", levels=None, window=None, interp=False, flush=False,
-             scale=None, grad="ste"):
+             scale=None, grad="ste_post"):
     """Attention backward over all heads: q, do (B, H, N, d); k, v (B, Hkv, N, d) float64.
     dK and dV of a KV head sum the shares of the query heads that read it."""
     B, H, N, d = q.shape

@@ -3,9 +3,13 @@
 The pages give no gradient formulas, so each mode is pinned by something other than the
 oracle's own algebra:
   * the exact kind, every mode: torch autograd through scaled_dot_product_attention;
-  * straight-through (ste), every kind: torch autograd through the straight-through
-    construction z = S + (log w - S).detach(), O = softmax(z) V, which gives the weight's
-    own derivative w in its score and the exact derivative of the normalisation;
+  * post-normalisation surrogate (ste_post), every kind: torch autograd through the
+    construction z = S + (log w - S).detach(), O = softmax(z) V, whose backward is that of
+    a softmax evaluated at the normalised weights;
+  * pre-normalisation surrogate and exact modes, attached and detached, every kind: torch
+    autograd through the forward rebuilt in torch from its definition (row max and min with
+    their gradients, the grid, the rounding passed straight through or held constant, the
+    normalisation), with the extrema detached in torch for the detached modes;
   * exact (almost-everywhere) gradients: central finite differences of the oracle forward;
   * exact_detached: central finite differences of the forward with the row extrema held at
     their unperturbed values (the oracle forward's ``extrema`` input).
@@ -35,7 +39,7 @@ def _qkvdo(B=1, H=2, Hkv=1, N=9, d=4, sigma=1.0, seed=0):
             r.standard_normal((B, Hkv, N, d)), r.standard_normal((B, H, N, d)))
 
 
-@pytest.mark.parametrize("grad", ["ste", "exact", "exact_detached"])
+@pytest.mark.parametrize("grad", ["ste_post", "ste_pre", "ste_pre_detached", "exact", "exact_detached"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_exact_kind_equals_sdpa_autograd(grad, causal):
     q, k, v, do = _qkvdo(H=4, Hkv=2, N=11, d=8, sigma=1.3, seed=1)
@@ -51,7 +55,7 @@ def test_exact_kind_equals_sdpa_autograd(grad, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_straight_through_equals_autograd_construction(var, causal):
     q, k, v, do = _qkvdo(N=10, d=4, sigma=1.6, seed=2)
-    r = oracle.attn_bwd(q, k, v, do, causal=causal, grad="ste", **var)
+    r = oracle.attn_bwd(q, k, v, do, causal=causal, grad="ste_post", **var)
     Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
     dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     N, d = q.shape[2], q.shape[3]
@@ -65,6 +69,101 @@ def test_straight_through_equals_autograd_construction(var, causal):
     np.testing.assert_allclose(r["dQ"], Q.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(r["dK"], K.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(r["dV"], V.grad.numpy(), atol=1e-12)
+
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def _torch_weights(S, vis, var, grad):
+    """The forward's weights rebuilt in torch (float64) so that autograd gives the
+    pre-normalisation surrogate (grad ste_pre*) or the exact derivative (exact*)."""
+    kind = var["kind"]
+    ste = grad.startswith("ste_pre")
+    neg_inf = torch.full_like(S, -math.inf)
+    m = torch.where(vis, S, neg_inf).max(dim=1).values            # gradient to the first arg-max
+    mn = torch.where(vis, S, -neg_inf).min(dim=1).values           # ... and the first arg-min
+    if grad.endswith("_detached"):
+        m, mn = m.detach(), mn.detach()
+    zero = torch.zeros_like(S)
+    if kind == "exact":
+        return torch.where(vis, torch.exp(S - m[:, None]), zero)
+    if kind in ("trunc", "uniform"):
+        kept = vis & ((m[:, None] - S).detach() <= var["window"])
+        val = torch.exp(S - m[:, None]) if kind == "trunc" else torch.ones_like(S)
+        return torch.where(kept, val, zero)
+    if kind == "pot":
+        L = var["levels"]
+        y = (m[:, None] - S) * LOG2E
+        r = torch.round(y.detach())                                  # half to even
+        pas = (r <= L - 1).double() if ste else 0.0
+        e = torch.clamp(r, max=L - 1) + (y - y.detach()) * pas
+        w = torch.exp2(-e)
+        if var.get("flush"):
+            w = torch.where(r <= L - 1, w, zero)
+        return torch.where(vis, w, zero)
+    K = var["levels"]
+    lo = (m - var["window"]) if "window" in var else mn
+    delta = (m - lo) / K
+    deg = (delta.detach() == 0)[:, None]          # a single visible score: every weight 1, no gradient
+    y = (m[:, None] - S) / torch.where(deg[:, 0], torch.ones_like(delta), delta)[:, None]
+    window = "window" in var
+    if var.get("interp"):
+        # past the grid's end (fixed windows only) the weight stays at T_K; at y = K the
+        # last interval's slope applies, and a min-max grid's arg-min (y = K up to
+        # rounding) is inside
+        yc = torch.where(y.detach() <= K, y, torch.full_like(y, float(K))) if window else y
+        l0 = torch.clamp(torch.floor(yc.detach()), 0, K - 1)
+        t = yc - l0
+        w = (1 - t) * torch.exp(-l0 * delta[:, None]) + t * torch.exp(-(l0 + 1) * delta[:, None])
+    else:
+        r = torch.round(y.detach())
+        pas = (r <= K).double() if ste else 0.0
+        lv = torch.clamp(r, max=K) + (y - y.detach()) * pas
+        w = torch.exp(-lv * delta[:, None])
+    if var.get("flush") and window:
+        w = torch.where(y.detach() <= K, w, zero)
+    w = torch.where(deg, torch.ones_like(w), w)
+    return torch.where(vis, w, zero)
+
+
+def _construction_grads(q, k, v, do, var, causal, grad):
+    Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    N, d = q.shape[2], q.shape[3]
+    vis = torch.ones(N, N, dtype=torch.bool)
+    if causal:
+        vis = torch.tril(vis)
+    group = q.shape[1] // k.shape[1]
+    for h in range(q.shape[1]):
+        S = (Q[0, h] @ K[0, h // group].T) / math.sqrt(d)
+        w = _torch_weights(S, vis, var, grad)
+        O = (w / w.sum(dim=1, keepdim=True)) @ V[0, h // group]
+        (O * torch.from_numpy(do[0, h])).sum().backward()
+    return tuple(np.zeros(t.shape) if t.grad is None else t.grad.numpy() for t in (Q, K, V))
+
+
+@pytest.mark.parametrize("grad", ["ste_pre", "ste_pre_detached", "exact", "exact_detached"])
+@pytest.mark.parametrize("var", KINDS, ids=_vid)
+@pytest.mark.parametrize("causal", [False, True])
+def test_modes_equal_autograd_through_the_rebuilt_forward(var, causal, grad):
+    q, k, v, do = _qkvdo(H=2, Hkv=1, N=10, d=4, sigma=1.6, seed=12)
+    r = oracle.attn_bwd(q, k, v, do, causal=causal, grad=grad, **var)
+    gq, gk, gv = _construction_grads(q, k, v, do, var, causal, grad)
+    np.testing.assert_allclose(r["dQ"], gq, atol=1e-12)
+    np.testing.assert_allclose(r["dK"], gk, atol=1e-12)
+    np.testing.assert_allclose(r["dV"], gv, atol=1e-12)
+
+
+def test_pre_surrogate_has_a_calibration_term_the_post_one_lacks():
+    # min-max hard rounding: dw/dDelta = w (y - l) moves the gradient of q and k
+    q, k, v, do = _qkvdo(N=8, d=4, sigma=1.5, seed=6)
+    var = dict(kind="kint", levels=4)
+    pre = oracle.attn_bwd(q, k, v, do, grad="ste_pre", **var)
+    post = oracle.attn_bwd(q, k, v, do, grad="ste_post", **var)
+    det = oracle.attn_bwd(q, k, v, do, grad="ste_pre_detached", **var)
+    assert np.abs(pre["dQ"] - post["dQ"]).max() > 1e-3
+    # with the extrema detached and nothing clipped (min-max: y <= K) the two placements agree
+    np.testing.assert_allclose(det["dQ"], post["dQ"], atol=1e-13)
+    np.testing.assert_allclose(det["dK"], post["dK"], atol=1e-13)
 
 
 def _fd(q, k, v, do, var, causal, extrema=None, h=1e-7):
@@ -142,6 +241,9 @@ import types
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "qsa_oracle.py")
 MUT_BWD = {
+    "ste_clip_ignored": ("dwdy = np.where(r <= K, -delta[:, None] * w, 0.0) if ste else np.zeros((R, N))",
+                         "dwdy = -delta[:, None] * w if ste else np.zeros((R, N))"),
+    "pot_ste_clip_ignored": ("g = np.where(visible & (e <= levels - 1), dw * w, 0.0)", "g = np.where(visible, dw * w, 0.0)"),
     "ste_drops_D": ("dS = np.where(visible, P * (dP - D[:, None]), 0.0)", "dS = np.where(visible, P * dP, 0.0)"),
     "dlo_sign": ("dlo = -dD / levels", "dlo = dD / levels"),
     "interp_slope_sign": ("dwdy = np.where(inside, T[rows, l0 + 1] - T[rows, l0], 0.0)",
@@ -161,8 +263,14 @@ def _bwd_checks(o):
             gq, gk, gv = _fd(q, k, v, do, var, False)
             np.testing.assert_allclose(r["dQ"], gq, atol=2e-6)
             np.testing.assert_allclose(r["dK"], gk, atol=2e-6)
+        for var in (dict(kind="kint", levels=4), dict(kind="kint", levels=3, window=1.5),
+                    dict(kind="pot", levels=3)):
+            r = o.attn_bwd(q, k, v, do, grad="ste_pre", **var)
+            gq, gk, gv = _construction_grads(q, k, v, do, var, False, "ste_pre")
+            np.testing.assert_allclose(r["dQ"], gq, atol=1e-12)
+            np.testing.assert_allclose(r["dK"], gk, atol=1e-12)
         var = dict(kind="pot", levels=4)
-        r = o.attn_bwd(q, k, v, do, grad="ste", **var)
+        r = o.attn_bwd(q, k, v, do, grad="ste_post", **var)
         Q, K = torch.tensor(q, requires_grad=True), torch.tensor(k, requires_grad=True)
         for h in range(2):
             S = (Q[0, h] @ K[0, 0].T) / math.sqrt(3)
