@@ -3,6 +3,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload fp8_8k] [--dtype fp8|bf16]
                     [--kind pot --levels 16] [--causal] [--no-cpu-baseline] [--no-variants]
+    python bench.py --backward      (the attention backward: its own JSON line)
+    python bench.py --energy        (board energy per forward: its own JSON line)
 
 A step is one call of the whole fused forward (row-extrema pre-pass, score
 tiles, weight formation, PV, epilogue) over the workload's full batch, with
@@ -252,6 +254,98 @@ def energy_run(args):
     return 0
 
 
+BWD_FLOPS_PER_PAIR_D = 10   # algorithmic backward: S recompute, dP, dV, dK, dQ (2 d flops each per pair)
+
+
+def bwd_executed_flops_per_pair(d, attached):
+    """fp32 FMA work the three backward launches execute per visible pair (2 flops per FMA):
+    rows 2 passes of (S, dP) plus one more when the extrema are attached; keys S, dP, dV, dK;
+    dQ S, dP, dQ."""
+    return 2 * d * ((6 if attached else 4) + 4 + 3)
+
+
+def cpu_baseline_bwd(wl, x, do, var, grad, budget_s):
+    """The float64 oracle backward on whole heads of the same inputs until `budget_s` seconds,
+    scaled to credited TFLOP/s (10 d flops per visible pair)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    B, H, N, d = x.q.shape
+    group = H // x.k.shape[1]
+    dec = lambda t: (oracle.decode_bf16(qin.raw_bits(t)) if t.dtype == torch.bfloat16  # noqa: E731
+                     else oracle.decode_f32(qin.raw_bits(t))).reshape(N, d)
+    t0 = time.perf_counter()
+    heads = 0
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        oracle.head_bwd(dec(x.q[b, h]), dec(x.k[b, h // group]), dec(x.v[b, h // group]), dec(do[b, h]),
+                        causal=wl.causal, grad=grad, **var)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    P = heads * (N * (N + 1) // 2 if wl.causal else N * N)
+    return {"value": round(BWD_FLOPS_PER_PAIR_D * d * P / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} whole head(s) ({N} queries x {N} keys) of the same workload, {el:.1f} s, float64 "
+                      f"NumPy; rate scaled to credited TFLOP/s (10 d flops per visible pair)"}
+
+
+def backward_run(args):
+    """The attention backward (qsa_attn_bwd: three fp32 launches) on the GPT-2-small shaped
+    pretraining attention (B 8, H 12, N 1024, d 64, bf16, causal), K-interval K = 4 with min-max
+    calibration and hard rounding through the pre-normalisation surrogate, plus a table of
+    other kinds and gradient modes."""
+    wl = qin.WORKLOADS["gpt2"]
+    x = qin.make_inputs(wl)
+    do = qin.make_dout(wl)
+    q, k, v, g = (t.cuda() for t in (x.q, x.k, x.v, do))
+    B, H, N, d = x.q.shape
+    P = pairs(B, H, N, wl.causal)
+    head = ({"kind": "kint", "levels": 4}, "ste_pre")
+    fn = lambda var, grad: qsa.attn_bwd(q, k, v, g, causal=wl.causal, grad=grad, **var)  # noqa: E731
+    print("[bwd] timing the headline", file=sys.stderr, flush=True)
+    ms, wall = time_loop(lambda: fn(*head), args.steps, args.warmup)
+    credited = BWD_FLOPS_PER_PAIR_D * d * P
+    tflops = credited / (ms * 1e-3) / 1e12
+    executed = bwd_executed_flops_per_pair(d, True) * P
+    rec = {
+        "metric": "attention bwd TFLOP/s (credited 10 d flops per visible pair)", "value": round(tflops, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "Hkv": x.k.shape[1], "N": N, "d": d, "causal": wl.causal,
+                   "inputs": "bf16", "variant": head[0], "grad": head[1], "parallelism": "single GPU"},
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_TFLOPS["f32"], 4), "traffic": None,
+                     "flops_per_launch": credited, "flops_per_pair": BWD_FLOPS_PER_PAIR_D * d,
+                     "executed_flops_per_pair": bwd_executed_flops_per_pair(d, True),
+                     "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 3),
+                     "note": "the three launches of one call timed together (HIP events); fp32 vector FMA peak"},
+    }
+    table = {}
+    for name, var, grad in [("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_post"),
+                            ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_pre_detached"),
+                            ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "exact"),
+                            ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True},
+                             "ste_pre"),
+                            ("kint4_window8_hard", {"kind": "kint", "levels": 4, "window": 8.0}, "ste_post"),
+                            ("pot8", {"kind": "pot", "levels": 8}, "ste_pre"),
+                            ("exact", {"kind": "exact"}, "ste_post")]:
+        print(f"[bwd] {name} {grad}", file=sys.stderr, flush=True)
+        t, host = time_calls(lambda: fn(var, grad), args.variant_calls // 4 or 5)
+        med = float(np.median(t))
+        table[f"{name}:{grad}"] = {"median_ms": round(med, 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+                                   "p90_ms": round(float(np.percentile(t, 90)), 5), "host_call_ms": round(host, 5),
+                                   "tflops": round(credited / (med * 1e-3) / 1e12, 3)}
+    rec["variants"] = table
+    if not args.no_cpu_baseline:
+        print("[bwd] oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_bwd(wl, x, do, head[0], head[1], args.cpu_seconds)
+    print(json.dumps(rec))
+    return 0
+
+
 def traffic_for(workload, dtype, var, causal, per_launch_flops):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources."""
@@ -291,6 +385,10 @@ def main(argv=None):
                          "workload, PoT against the exact kinds (amdsmi energy counter)")
     ap.add_argument("--energy-seconds", type=float, default=2.0)
     ap.add_argument("--energy-rounds", type=int, default=2)
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward line: the attention backward on the GPT-2-small shaped "
+                         "pretraining attention (bf16, causal), K-interval K=4 through the pre-normalisation "
+                         "surrogate, with a table of other kinds and gradient modes")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-kernel: also run a plain device copy of this many bytes `steps` times "
                          "(the known-size reference for HBM traffic counters)")
@@ -306,6 +404,8 @@ def main(argv=None):
 
     if args.energy:
         return energy_run(args)
+    if args.backward:
+        return backward_run(args)
     wl = qin.WORKLOADS[args.workload]
     if args.dtype:
         wl = wl.replace(dtype=args.dtype)

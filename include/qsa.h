@@ -1,8 +1,8 @@
 /*
- * qsa.h -- C ABI of libqsa, the quantized-softmax attention forward for
- * AMD Instinct MI355X (gfx950).
+ * qsa.h -- C ABI of libqsa, the quantized-softmax attention forward (and its
+ * backward) for AMD Instinct MI355X (gfx950).
  *
- * One operation: the fused attention forward
+ * The main operation: the fused attention forward
  *
  *     O = softmax~(scale * Q K^T) V
  *
@@ -107,7 +107,9 @@ typedef enum {
  * QSA_F_WINDOW        K-interval only: fixed-window calibration [m - window, m].
  * QSA_F_FLUSH         K-interval (window) and PoT: scores outside the grid
  *                     (K-interval: s < m - window; PoT: e >= L) get weight 0
- *                     instead of the last grid value.
+ *                     instead of the last grid value.  On a min-max K-interval
+ *                     grid every visible score lies inside, so the flag is
+ *                     accepted and changes nothing.
  *
  * rint is round-half-to-even.  The row maximum always gets weight exactly 1.
  */
@@ -197,6 +199,67 @@ int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O,
                     int B, int H, int Hkv, int N, int d, int causal,
                     int variant, int k_levels, float window, int dtype,
                     const qsa_fwd_ex_opts* opts, void* stream);
+
+/*
+ * Gradient modes of qsa_attn_bwd.  "Pretraining Transformers with Quantized
+ * Softmax in Attention" (abstract; chapter 5 "Build the method") trains
+ * K-interval attention with a straight-through surrogate placed before or
+ * after the normalisation, derives backward rules through the calibration,
+ * and compares attached with detached row extrema; it prints no formulas, so
+ * each mode below states its reading.  P = w / l, dP = dO V^T, D_i = dO_i . O_i.
+ *
+ * QSA_GRAD_STE_POST        surrogate after the normalisation: P is passed back
+ *                          as a softmax of the scores, dS = P (dP - D).
+ * QSA_GRAD_EXACT           the derivative of the forward wherever it exists:
+ *                          through each score (interpolation: the grid line's
+ *                          slope; hard rounding, PoT, uniform: 0; exponential
+ *                          kinds: w) and through the calibration (m moves y and,
+ *                          for min-max grids, Delta = (m - lo)/K and the grid
+ *                          values; lo moves Delta), those two gradients landing
+ *                          on the row's first arg-max and arg-min keys.
+ * QSA_GRAD_EXACT_DETACHED  QSA_GRAD_EXACT with m and lo held constant.
+ * QSA_GRAD_STE_PRE         surrogate before the normalisation: QSA_GRAD_EXACT
+ *                          with the rounding of the grid coordinate (K-interval
+ *                          hard rounding, PoT) passed straight through where the
+ *                          clip to the last level is not active.
+ * QSA_GRAD_STE_PRE_DETACHED  QSA_GRAD_STE_PRE with m and lo held constant.
+ *
+ * At y = K the last interval's slope applies; on a min-max grid every visible
+ * key counts as inside it.  A min-max row whose visible scores are all equal
+ * gets no gradient through its weights in the modes other than STE_POST.
+ */
+enum {
+  QSA_GRAD_STE_POST = 0,
+  QSA_GRAD_EXACT = 1,
+  QSA_GRAD_EXACT_DETACHED = 2,
+  QSA_GRAD_STE_PRE = 3,
+  QSA_GRAD_STE_PRE_DETACHED = 4
+};
+
+/*
+ * qsa_attn_bwd -- gradients of sum(dO * O) for O = qsa_attn_fwd(Q, K, V, ...).
+ *
+ *   Q, K, V, dO  device inputs: Q and dO [B, H, N, d], K and V [B, Hkv, N, d],
+ *                one dtype, QSA_DT_F32 or QSA_DT_BF16 (QSA_DT_FP8_E4M3 returns
+ *                QSA_ERR_UNSUPPORTED).
+ *   dQ           device output [B, H, N, d] float32.  Also the workspace: the
+ *                first launch parks 8 floats of per-row constants at the start
+ *                of each row of dQ, which the last launch reads and overwrites.
+ *   dK, dV       device outputs [B, Hkv, N, d] float32, summed over the query
+ *                heads of each KV head (overwritten, not accumulated).
+ *   B .. dtype   as for qsa_attn_fwd (same limits, kinds and flags).
+ *   grad         a QSA_GRAD_* mode.
+ *   scale        score scale; 0 -> 1/sqrt(d).
+ *   stream       hipStream_t or NULL.
+ * dQ, dK and dV must not overlap each other or the inputs.  The forward's O is
+ * not needed: the call recomputes the weights from Q and K (three kernels on
+ * `stream`).  Float32 arithmetic throughout.  Returns a qsa_status.
+ */
+int qsa_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
+                 float* dQ, float* dK, float* dV,
+                 int B, int H, int Hkv, int N, int d, int causal,
+                 int variant, int k_levels, float window, int dtype,
+                 int grad, float scale, void* stream);
 
 /* Host-only validation of the scalar arguments of qsa_attn_fwd (no HIP call,
  * no pointer check).  Returns the status qsa_attn_fwd would return. */

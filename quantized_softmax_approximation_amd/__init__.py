@@ -1,4 +1,4 @@
-"""Quantized-softmax attention forward for AMD Instinct MI355X (gfx950).
+"""Quantized-softmax attention forward (and backward) for AMD Instinct MI355X (gfx950).
 
 A thin ctypes binding over libqsa.so (C ABI in include/qsa.h).  Every step of
 the computation runs in the library's HIP kernels; this module only checks
@@ -7,6 +7,7 @@ non-zero status.  PyTorch provides device memory and streams.
 
     import quantized_softmax_approximation_amd as qsa
     o = qsa.attn_fwd(q, k, v, causal=True, kind="pot", levels=8)
+    dq, dk, dv = qsa.attn_bwd(q, k, v, do, causal=True, kind="kint", levels=4, grad="ste_pre")
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_validate", "variant_code", "status_string", "last_error",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_validate", "GRADS", "variant_code", "status_string", "last_error",
            "version", "lib", "lib_path", "QSAError", "EXACT", "KINT", "POT", "EXACT_ANCHORED", "TRUNC", "UNIFORM", "F_INTERP",
            "F_WINDOW", "F_FLUSH", "DT_F32", "DT_BF16", "DT_FP8_E4M3", "IDX_FLUSHED", "IDX_MASKED"]
 
@@ -27,6 +28,9 @@ DT_F32, DT_BF16, DT_FP8_E4M3 = 0, 1, 2
 EXACT, KINT, POT, EXACT_ANCHORED, TRUNC, UNIFORM = 0, 1, 2, 3, 4, 5
 F_INTERP, F_WINDOW, F_FLUSH = 1 << 4, 1 << 5, 1 << 6
 IDX_FLUSHED, IDX_MASKED = 254, 255
+GRAD_STE_POST, GRAD_EXACT, GRAD_EXACT_DETACHED, GRAD_STE_PRE, GRAD_STE_PRE_DETACHED = range(5)
+GRADS = {"ste_post": GRAD_STE_POST, "exact": GRAD_EXACT, "exact_detached": GRAD_EXACT_DETACHED,
+         "ste_pre": GRAD_STE_PRE, "ste_pre_detached": GRAD_STE_PRE_DETACHED}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
@@ -62,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_attn_fwd.restype = i
         L.qsa_attn_fwd_ex.argtypes = [p, p, p, p, i, i, i, i, i, i, i, i, f, i, ctypes.POINTER(_Opts), p]
         L.qsa_attn_fwd_ex.restype = i
+        L.qsa_attn_bwd.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, i, f, p]
+        L.qsa_attn_bwd.restype = i
         L.qsa_attn_validate.argtypes = [i, i, i, i, i, i, i, i, f, i]
         L.qsa_attn_validate.restype = i
         L.qsa_status_string.argtypes = [i]
@@ -193,3 +199,40 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
     if status != OK:
         raise QSAError(status, last_error())
     return out
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, do: torch.Tensor, *, causal: bool = False,
+             kind: str = "exact", levels: int = 0, window: Optional[float] = None, interp: bool = False,
+             flush: bool = False, grad: str = "ste_post", scale: float = 0.0,
+             stream: Optional[torch.cuda.Stream] = None):
+    """Gradients (dq, dk, dv) of sum(do * O) through qsa_attn_bwd, O being attn_fwd of the
+    same arguments.  q, do: [B,H,N,d]; k, v: [B,Hkv,N,d]; one dtype, float32 or bfloat16,
+    contiguous, on one GPU.  The gradients are float32 (dk, dv summed over each KV head's
+    query heads).  grad: one of GRADS.  Asynchronous on `stream` (default: the current one).
+    """
+    if grad not in GRADS:
+        raise ValueError(f"grad must be one of {sorted(GRADS)}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d) or tuple(do.shape) != (B, H, N, d):
+        raise ValueError("k, v must be [B, Hkv, N, d] and do [B, H, N, d]")
+    if not (q.dtype == k.dtype == v.dtype == do.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q, k, v, do must share one dtype, float32 or bfloat16")
+    dev = q.device
+    if k.device != dev or v.device != dev or do.device != dev:
+        raise ValueError("q, k, v, do must be on the same GPU")
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+    variant = variant_code(kind, interp=interp, window=window, flush=flush)
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    with torch.cuda.device(dev):
+        status = lib().qsa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv,
+                                    N, d, int(bool(causal)), variant, int(levels), float(window or 0.0), _DT[q.dtype],
+                                    GRADS[grad], float(scale), ctypes.c_void_p(st))
+    if status != OK:
+        raise QSAError(status, last_error())
+    return dq, dk, dv

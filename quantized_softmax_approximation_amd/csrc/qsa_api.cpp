@@ -70,7 +70,10 @@ int validate(int B, int H, int Hkv, int N, int d, int causal, int variant, int k
 
 int weight_kind(int variant) {
   const int base = variant & QSA_BASE_MASK;
-  const bool flush = variant & QSA_F_FLUSH, interp = variant & QSA_F_INTERP;
+  const bool interp = variant & QSA_F_INTERP;
+  // a min-max grid spans every visible score, so flushing removes nothing there; dropping the
+  // flag keeps a rounded y = K + ulp at the row minimum from flushing the arg-min key
+  const bool flush = (variant & QSA_F_FLUSH) && !(base == QSA_KINT && !(variant & QSA_F_WINDOW));
   switch (base) {
     case QSA_EXACT: return qsa::WK_EXACT;
     case QSA_EXACT_ANCHORED: return qsa::WK_EXACT_ANCH;
@@ -162,6 +165,44 @@ int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, int B,
 int qsa_attn_fwd(const void* Q, const void* K, const void* V, void* O, int B, int H, int Hkv, int N, int d,
                  int causal, int variant, int k_levels, float window, int dtype, void* stream) {
   return qsa_attn_fwd_ex(Q, K, V, O, B, H, Hkv, N, d, causal, variant, k_levels, window, dtype, nullptr, stream);
+}
+
+int qsa_attn_bwd(const void* Q, const void* K, const void* V, const void* dO, float* dQ, float* dK, float* dV, int B,
+                 int H, int Hkv, int N, int d, int causal, int variant, int k_levels, float window, int dtype, int grad,
+                 float scale, void* stream) {
+  int st = validate(B, H, Hkv, N, d, causal, variant, k_levels, window, dtype);
+  if (st != QSA_OK) return st;
+  if (dtype == QSA_DT_FP8_E4M3) return fail(QSA_ERR_UNSUPPORTED, "the backward takes float32 or bfloat16 inputs");
+  if (grad < QSA_GRAD_STE_POST || grad > QSA_GRAD_STE_PRE_DETACHED)
+    return fail(QSA_ERR_PARAM, "unknown gradient mode %d", grad);
+  if (!(std::isfinite(scale) && scale >= 0.0f))
+    return fail(QSA_ERR_PARAM, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
+    return fail(QSA_ERR_NULL_PTR, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
+  const int base = variant & QSA_BASE_MASK;
+  qsa::BwdArgs a = {};
+  a.f.q = Q;
+  a.f.k = K;
+  a.f.v = V;
+  a.f.B = B;
+  a.f.H = H;
+  a.f.Hkv = Hkv;
+  a.f.N = N;
+  a.f.causal = causal ? 1 : 0;
+  a.f.levels = k_levels;
+  a.f.window_calib = (base == QSA_KINT && (variant & QSA_F_WINDOW)) ? 1 : 0;
+  a.f.window = (a.f.window_calib || base == QSA_TRUNC || base == QSA_UNIFORM) ? window : 0.0f;
+  a.f.sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)d);
+  a.f.vd = 1.0f;
+  a.dout = dO;
+  a.dq = dQ;
+  a.dk = dK;
+  a.dv = dV;
+  a.mode = grad;
+  a.bf16 = dtype == QSA_DT_BF16 ? 1 : 0;
+  const hipError_t e = qsa::launch_bwd(a, d, weight_kind(variant), (hipStream_t)stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 const char* qsa_status_string(int status) {

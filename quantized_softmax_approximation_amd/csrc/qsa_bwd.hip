@@ -1,0 +1,467 @@
+// Quantized-softmax attention backward: dQ, dK, dV of sum(dO * O), float32 math.
+//
+// Gradient modes.  The pages train K-interval attention with a straight-through surrogate whose
+// placement relative to the normalisation they vary, derive backward rules that include the
+// derivatives through the calibration, and compare attached with detached row extrema
+// ("Pretraining Transformers with Quantized Softmax in Attention", abstract; chapter 5 "Build
+// the method").  They print no formulas, so the modes are readings:
+//   0 post-normalisation surrogate: P = w / l is passed back as a softmax of the scores,
+//     dS = P (dP - D) with dP = dO V^T and D_i = dO_i . O_i; the extrema do not enter.
+//   1 exact: the derivative of the forward function wherever it exists.  Through each score
+//     directly (the slope of the interpolated grid line; zero for hard rounding, PoT and
+//     uniform weights; w itself for the exponential kinds) and through the calibration: the
+//     row maximum m moves y = (m - s)/Delta and, for min-max grids, Delta = (m - lo)/K, and the
+//     row minimum lo moves Delta and with it the grid values T_l = exp(-l Delta).  Those two
+//     gradients land on the row's arg-max and arg-min keys (first in key order).
+//   2 exact with m and lo held constant (detached extrema).
+//   3 pre-normalisation surrogate: as 1, but the rounding of the grid coordinate (K-interval
+//     hard rounding, PoT) is passed straight through where the clip to the last level is not
+//     active, so hard rounding gets dw/ds = w and the calibration term dw/dDelta = w (y - l).
+//   4 as 3 with the extrema detached.
+//
+// A correctness path like the float32 forward, not a tuned one: four lanes per query row or
+// key (lane u of a quad holds dimensions u, u+4, ..., so quads read LDS without bank
+// conflicts), fp32 FMAs, 64-row or 64-key tiles staged in LDS.  Three launches on the caller's
+// stream:
+//   bwd_rows  per query row: the extrema and their keys, l, D and (attached modes) the
+//             gradients of m and lo, parked in the first 8 floats of the row's dQ;
+//   bwd_keys  per key: dK and dV, summed over the query heads that read the key's KV head;
+//   bwd_dq    per query row: dQ (it reads its parked constants, then overwrites the row).
+// Every launch computes scores with the same operation order, so the three agree exactly on
+// every weight.
+#include "qsa_common.h"
+#include "qsa_weights.h"
+
+namespace qsa {
+namespace {
+
+constexpr int TB = 64;   // rows or keys per workgroup (one quad each)
+constexpr int SHB = 8;   // K-interval table row shift: log2(TB * 4)
+constexpr int NPARK = 8; // floats parked per row: M, MN, l, D, dm, dlo, arg-max, arg-min
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p) {
+  return (float)*p;
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+// x . row for the quad: lane u multiplies dimensions u, u+4, ... then the quad adds up
+template <int D>
+__device__ __forceinline__ float qdot(const float* row, const float (&x)[D / 4], int u) {
+  float p = 0.0f;
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) p = fmaf(x[k], row[4 * k + u], p);
+  return quad_sum(p);
+}
+
+// Gradient modes (the values of BwdArgs::mode)
+constexpr int G_STE_POST = 0, G_EXACT = 1, G_EXACT_DET = 2, G_STE_PRE = 3, G_STE_PRE_DET = 4;
+__device__ __forceinline__ bool g_ste(int mode) { return mode == G_STE_PRE || mode == G_STE_PRE_DET; }
+__device__ __forceinline__ bool g_attached(int mode) { return mode == G_EXACT || mode == G_STE_PRE; }
+
+// Per-element derivatives of the weight for the exact and pre-normalisation surrogate modes:
+// gs = dw/ds (direct, score units), cm = dw/dm, clo = dw/dlo.  dsc: grid step Delta in score
+// units (K-interval).  STE: the rounding of the grid coordinate is passed straight through
+// where the clip to the last level is not active.  At y = K the last interval's slope applies,
+// and on a min-max grid every visible key is inside (its arg-min sits on y = K up to rounding).
+template <int WK>
+__device__ __forceinline__ void partials(float acc, float w, const RowC& rc, const unsigned char* Tb, int K,
+                                         float dsc, bool minmax, bool ste, float& gs, float& cm, float& clo) {
+  gs = cm = clo = 0.0f;
+  if (WK == WK_EXACT || WK == WK_EXACT_ANCH || WK == WK_TRUNC) {  // w = exp(s - m) where kept
+    gs = w;
+    cm = -w;
+    return;
+  }
+  if (WK == WK_POT || WK == WK_POT_FLUSH) {  // 2^-e with e := y = (m - s) log2(e) inside the clip
+    if (ste && __builtin_rintf(fmaf(acc, -rc.c, rc.mc)) <= (float)(K - 1)) {
+      gs = w;
+      cm = -w;
+    }
+    return;
+  }
+  if (!wk_kint(WK) || rc.c == 0.0f) return;  // uniform weights, zero-width grids
+  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH);
+  constexpr bool FLUSH = (WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);  // fixed-window grids only
+  const float y = fmaf(acc, -rc.c, rc.mc);  // (m - s) / Delta
+  const float Kf = (float)K;
+  float dwdy = 0.0f, dwdD = 0.0f;           // dw/dy, and dw/dDelta at fixed y
+  if (INTERP) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    if (minmax || y <= Kf) {
+      const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, Kf);
+      const float lf = fminf(__builtin_floorf(yc), Kf - 1.0f);
+      const uint32_t l = (uint32_t)(int32_t)lf;
+      const float t = yc - lf;
+      const f2 e = *(const f2*)(Tb + ((l << (SHB + 1)) + rc.tab));  // (T_l, T_l+1 - T_l)
+      dwdy = e.y;
+      dwdD = (1.0f - t) * (-lf * e.x) + t * (-(lf + 1.0f) * (e.x + e.y));
+    } else if (!FLUSH) {
+      const f2 e = *(const f2*)(Tb + (((uint32_t)K << (SHB + 1)) + rc.tab));
+      dwdD = -Kf * e.x;
+    }
+  } else {
+    const float r = __builtin_rintf(fmaxf(y, 0.0f));
+    if (!(FLUSH && y > Kf)) {
+      const float lf = fminf(r, Kf);
+      const float tl = *(const float*)(Tb + ((((uint32_t)(int32_t)lf) << SHB) + rc.tab));
+      dwdD = -lf * tl;
+      if (ste && r <= Kf) dwdy = -dsc * w;  // T_l = exp(-l Delta) with l := y
+    }
+  }
+  const float inv = 1.0f / dsc;
+  gs = -dwdy * inv;
+  const float dD = dwdD - dwdy * y * inv;  // total dw/dDelta with y moving with Delta
+  cm = dwdy * inv + (minmax ? dD / Kf : 0.0f);
+  clo = minmax ? -dD / Kf : 0.0f;
+}
+
+// Grid step in score units (K-interval), from the row extrema in raw units.
+__device__ __forceinline__ float grid_step(const FwdArgs& f, float M, float MN) {
+  return f.window_calib ? f.window / (float)f.levels : (M - MN) * f.sc / (float)f.levels;
+}
+
+template <typename T, int D, int WK>
+__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  constexpr int DL = D / 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Ks = (float*)smem;
+  float* Vs = Ks + TB * D;
+  unsigned char* Tb = (unsigned char*)(Vs + TB * D);
+
+  const int tid = threadIdx.x, rl = tid >> 2, u = tid & 3;
+  int bh, qt;
+  map_block(f, bh, qt);
+  const int b = bh / f.H, h = bh - b * f.H;
+  const int kvh = h / (f.H / f.Hkv);
+  const int N = f.N;
+  const int row = qt * TB + rl;
+  const T* Qg = (const T*)f.q + (size_t)(b * f.H + h) * N * D;
+  const T* Gg = (const T*)a.dout + (size_t)(b * f.H + h) * N * D;
+  const T* Kg = (const T*)f.k + (size_t)(b * f.Hkv + kvh) * N * D;
+  const T* Vg = (const T*)f.v + (size_t)(b * f.Hkv + kvh) * N * D;
+
+  float q[DL], g[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) {
+    q[k] = row < N ? ld(Qg + (size_t)row * D + 4 * k + u) : 0.0f;
+    g[k] = row < N ? ld(Gg + (size_t)row * D + 4 * k + u) : 0.0f;
+  }
+  const int kt_end = f.causal ? ((min(qt * TB + TB, N) - 1) / TB + 1) : (N + TB - 1) / TB;
+  const int lim = row < N ? (f.causal ? row : N - 1) : -1;  // last key this row sees
+  auto load_tile = [&](float* dst, const T* src, int kt) {
+    for (int e = tid; e < TB * D; e += 256) {
+      const int key = kt * TB + e / D;
+      dst[e] = key < N ? ld(src + (size_t)key * D + e % D) : 0.0f;
+    }
+  };
+
+  // extrema over the visible keys and the first keys that reach them
+  float M = -__builtin_inff(), MN = __builtin_inff();
+  int amax = -1, amin = -1;
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();
+    load_tile(Ks, Kg, kt);
+    __syncthreads();
+    for (int j = 0; j < TB; ++j) {
+      const int key = kt * TB + j;
+      const float s = qdot<D>(Ks + j * D, q, u);
+      if (key <= lim) {
+        if (s > M) { M = s; amax = key; }
+        if (s < MN) { MN = s; amin = key; }
+      }
+    }
+  }
+  if (row >= N) M = MN = 0.0f;
+  const RowC rc = make_row<WK, SHB>(f, M, MN, rl, Tb, u, 4);
+  const float dsc = wk_kint(WK) ? grid_step(f, M, MN) : 1.0f;
+  const bool minmax = wk_kint(WK) && !f.window_calib;
+
+  // l and D = sum_j P_ij dP_ij (= dO_i . O_i)
+  float l = 0.0f, wdp = 0.0f;
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();
+    load_tile(Ks, Kg, kt);
+    load_tile(Vs, Vg, kt);
+    __syncthreads();
+    for (int j = 0; j < TB; ++j) {
+      const float s = qdot<D>(Ks + j * D, q, u);
+      const float dp = qdot<D>(Vs + j * D, g, u);
+      if (kt * TB + j <= lim) {
+        const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
+        l += w;
+        wdp = fmaf(w, dp, wdp);
+      }
+    }
+  }
+  const float Dr = row < N ? wdp / l : 0.0f;
+
+  // extrema attached: the gradients of m and lo
+  float dm = 0.0f, dlo = 0.0f;
+  if (g_attached(a.mode) && (WK == WK_TRUNC || wk_kint(WK) || ((WK == WK_POT || WK == WK_POT_FLUSH) && g_ste(a.mode)))) {
+    for (int kt = 0; kt < kt_end; ++kt) {
+      __syncthreads();
+      load_tile(Ks, Kg, kt);
+      load_tile(Vs, Vg, kt);
+      __syncthreads();
+      for (int j = 0; j < TB; ++j) {
+        const float s = qdot<D>(Ks + j * D, q, u);
+        const float dp = qdot<D>(Vs + j * D, g, u);
+        if (kt * TB + j <= lim) {
+          const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
+          float gs, cm, clo;
+          partials<WK>(s, w, rc, Tb, f.levels, dsc, minmax, g_ste(a.mode), gs, cm, clo);
+          const float dw = (dp - Dr) / l;
+          dm = fmaf(dw, cm, dm);
+          dlo = fmaf(dw, clo, dlo);
+        }
+      }
+    }
+  }
+  if (row < N && u == 0) {
+    float* pk = a.dq + ((size_t)(b * f.H + h) * N + row) * D;
+    pk[0] = M;
+    pk[1] = MN;
+    pk[2] = l;
+    pk[3] = Dr;
+    pk[4] = dm;
+    pk[5] = dlo;
+    pk[6] = __builtin_bit_cast(float, amax);
+    pk[7] = __builtin_bit_cast(float, amin);
+  }
+}
+
+// dS_ij from the weight, the row constants and dP_ij (modes as in the file header)
+template <int WK>
+__device__ __forceinline__ float dscore(int mode, float s, float w, float dp, int key, const RowC& rc,
+                                        const unsigned char* Tb, const FwdArgs& f, float l, float Dr, float dm,
+                                        float dlo, int amax, int amin, float dsc, bool minmax) {
+  if (mode == G_STE_POST) return (w / l) * (dp - Dr);
+  float gs, cm, clo;
+  partials<WK>(s, w, rc, Tb, f.levels, dsc, minmax, g_ste(mode), gs, cm, clo);
+  float ds = (dp - Dr) / l * gs;
+  if (g_attached(mode)) {
+    if (key == amax) ds += dm;
+    if (key == amin && minmax) ds += dlo;
+  }
+  return ds;
+}
+
+template <typename T, int D, int WK>
+__global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  constexpr int DL = D / 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Qs = (float*)smem;
+  float* Gs = Qs + TB * D;
+  float* Rp = Gs + TB * D;                               // [TB][NPARK] parked row constants
+  RowC* Rc = (RowC*)(Rp + TB * NPARK);                   // [TB] row constants
+  unsigned char* Tb = (unsigned char*)(Rc + TB);
+
+  const int tid = threadIdx.x, kl = tid >> 2, u = tid & 3;
+  const int N = f.N, nt = (N + TB - 1) / TB;
+  const int kt = blockIdx.x % nt, bkv = blockIdx.x / nt;
+  const int b = bkv / f.Hkv, kvh = bkv - b * f.Hkv;
+  const int group = f.H / f.Hkv;
+  const int key = kt * TB + kl;
+  const T* Kg = (const T*)f.k + (size_t)(b * f.Hkv + kvh) * N * D;
+  const T* Vg = (const T*)f.v + (size_t)(b * f.Hkv + kvh) * N * D;
+  float kk[DL], vv[DL], dk[DL], dv[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) {
+    kk[k] = key < N ? ld(Kg + (size_t)key * D + 4 * k + u) : 0.0f;
+    vv[k] = key < N ? ld(Vg + (size_t)key * D + 4 * k + u) : 0.0f;
+    dk[k] = dv[k] = 0.0f;
+  }
+  const bool minmax = wk_kint(WK) && !f.window_calib;
+
+  for (int hq = kvh * group; hq < (kvh + 1) * group; ++hq) {
+    const T* Qg = (const T*)f.q + (size_t)(b * f.H + hq) * N * D;
+    const T* Gg = (const T*)a.dout + (size_t)(b * f.H + hq) * N * D;
+    const float* Pk = a.dq + (size_t)(b * f.H + hq) * N * D;
+    for (int qt = f.causal ? kt : 0; qt < nt; ++qt) {
+      __syncthreads();
+      for (int e = tid; e < TB * D; e += 256) {
+        const int r = qt * TB + e / D;
+        Qs[e] = r < N ? ld(Qg + (size_t)r * D + e % D) : 0.0f;
+        Gs[e] = r < N ? ld(Gg + (size_t)r * D + e % D) : 0.0f;
+      }
+      // quad kl takes row kl of the tile: its parked constants and its grid table
+      {
+        const int r = qt * TB + kl;
+        float pk[NPARK];
+#pragma unroll
+        for (int c = 0; c < NPARK; ++c) pk[c] = r < N ? Pk[(size_t)r * D + c] : 0.0f;
+        const RowC rc = make_row<WK, SHB>(f, pk[0], pk[1], kl, Tb, u, 4);
+        if (u == 0) {
+#pragma unroll
+          for (int c = 0; c < NPARK; ++c) Rp[kl * NPARK + c] = pk[c];
+          Rc[kl] = rc;
+        }
+      }
+      __syncthreads();
+      for (int r = 0; r < TB; ++r) {
+        const int i = qt * TB + r;
+        if (i >= N) break;
+        const float s = qdot<D>(Qs + r * D, kk, u);
+        const float dp = qdot<D>(Gs + r * D, vv, u);
+        if (key < N && (!f.causal || key <= i)) {
+          const RowC rc = Rc[r];
+          const float* pk = Rp + r * NPARK;
+          const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
+          const float l = pk[2];
+          const float dsc = wk_kint(WK) ? grid_step(f, pk[0], pk[1]) : 1.0f;
+          const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, l, pk[3], pk[4], pk[5],
+                                      __builtin_bit_cast(int, pk[6]), __builtin_bit_cast(int, pk[7]), dsc, minmax);
+          const float p = w / l;
+#pragma unroll
+          for (int k = 0; k < DL; ++k) {
+            dv[k] = fmaf(p, Gs[r * D + 4 * k + u], dv[k]);
+            dk[k] = fmaf(ds, Qs[r * D + 4 * k + u], dk[k]);
+          }
+        }
+      }
+    }
+  }
+  if (key < N) {
+    float* dKg = a.dk + ((size_t)(b * f.Hkv + kvh) * N + key) * D;
+    float* dVg = a.dv + ((size_t)(b * f.Hkv + kvh) * N + key) * D;
+#pragma unroll
+    for (int k = 0; k < DL; ++k) {
+      dKg[4 * k + u] = f.sc * dk[k];
+      dVg[4 * k + u] = dv[k];
+    }
+  }
+}
+
+template <typename T, int D, int WK>
+__global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
+  const FwdArgs& f = a.f;
+  constexpr int DL = D / 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Ks = (float*)smem;
+  float* Vs = Ks + TB * D;
+  unsigned char* Tb = (unsigned char*)(Vs + TB * D);
+
+  const int tid = threadIdx.x, rl = tid >> 2, u = tid & 3;
+  int bh, qt;
+  map_block(f, bh, qt);
+  const int b = bh / f.H, h = bh - b * f.H;
+  const int kvh = h / (f.H / f.Hkv);
+  const int N = f.N;
+  const int row = qt * TB + rl;
+  const T* Qg = (const T*)f.q + (size_t)(b * f.H + h) * N * D;
+  const T* Gg = (const T*)a.dout + (size_t)(b * f.H + h) * N * D;
+  const T* Kg = (const T*)f.k + (size_t)(b * f.Hkv + kvh) * N * D;
+  const T* Vg = (const T*)f.v + (size_t)(b * f.Hkv + kvh) * N * D;
+  float* dQg = a.dq + ((size_t)(b * f.H + h) * N + row) * D;
+
+  float q[DL], g[DL], dq[DL];
+  float pk[NPARK];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) {
+    q[k] = row < N ? ld(Qg + (size_t)row * D + 4 * k + u) : 0.0f;
+    g[k] = row < N ? ld(Gg + (size_t)row * D + 4 * k + u) : 0.0f;
+    dq[k] = 0.0f;
+  }
+#pragma unroll
+  for (int c = 0; c < NPARK; ++c) pk[c] = row < N ? dQg[c] : 0.0f;  // before the row is overwritten
+  const RowC rc = make_row<WK, SHB>(f, pk[0], pk[1], rl, Tb, u, 4);
+  const float dsc = wk_kint(WK) ? grid_step(f, pk[0], pk[1]) : 1.0f;
+  const bool minmax = wk_kint(WK) && !f.window_calib;
+  const int amax = __builtin_bit_cast(int, pk[6]), amin = __builtin_bit_cast(int, pk[7]);
+  const int kt_end = f.causal ? ((min(qt * TB + TB, N) - 1) / TB + 1) : (N + TB - 1) / TB;
+  const int lim = row < N ? (f.causal ? row : N - 1) : -1;
+  auto load_tile = [&](float* dst, const T* src, int kt) {
+    for (int e = tid; e < TB * D; e += 256) {
+      const int key = kt * TB + e / D;
+      dst[e] = key < N ? ld(src + (size_t)key * D + e % D) : 0.0f;
+    }
+  };
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();
+    load_tile(Ks, Kg, kt);
+    load_tile(Vs, Vg, kt);
+    __syncthreads();
+    for (int j = 0; j < TB; ++j) {
+      const int key = kt * TB + j;
+      const float s = qdot<D>(Ks + j * D, q, u);
+      const float dp = qdot<D>(Vs + j * D, g, u);
+      if (key <= lim) {
+        const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
+        const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, pk[2], pk[3], pk[4], pk[5], amax, amin,
+                                    dsc, minmax);
+#pragma unroll
+        for (int k = 0; k < DL; ++k) dq[k] = fmaf(ds, Ks[j * D + 4 * k + u], dq[k]);
+      }
+    }
+  }
+  if (row < N) {
+#pragma unroll
+    for (int k = 0; k < DL; ++k) dQg[4 * k + u] = f.sc * dq[k];
+  }
+}
+
+template <typename T, int D, int WK>
+hipError_t launch_typed(const BwdArgs& a0, hipStream_t st) {
+  BwdArgs a = a0;
+  a.f.n_qtiles = (a.f.N + TB - 1) / TB;
+  a.f.total_blocks = a.f.B * a.f.H * a.f.n_qtiles;
+  const size_t tab = table_bytes(WK, TB, a.f.levels);
+  const size_t lds_rows = 2 * (size_t)TB * D * 4 + tab;
+  const size_t lds_keys = 2 * (size_t)TB * D * 4 + (size_t)TB * NPARK * 4 + (size_t)TB * sizeof(RowC) + tab;
+  const void* ks[3] = {(const void*)bwd_rows<T, D, WK>, (const void*)bwd_keys<T, D, WK>, (const void*)bwd_dq<T, D, WK>};
+  const size_t lds[3] = {lds_rows, lds_keys, lds_rows};
+  for (int i = 0; i < 3; ++i)
+    if (lds[i] > 65536) {
+      const hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
+      if (e != hipSuccess) return e;
+    }
+  hipLaunchKernelGGL((bwd_rows<T, D, WK>), dim3(a.f.total_blocks), dim3(256), lds_rows, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int key_blocks = a.f.B * a.f.Hkv * ((a.f.N + TB - 1) / TB);
+  hipLaunchKernelGGL((bwd_keys<T, D, WK>), dim3(key_blocks), dim3(256), lds_keys, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq<T, D, WK>), dim3(a.f.total_blocks), dim3(256), lds_rows, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_kind(const BwdArgs& a, int wk, hipStream_t st) {
+  switch (wk) {
+    case WK_EXACT:
+    case WK_EXACT_ANCH: return launch_typed<T, D, WK_EXACT_ANCH>(a, st);  // the same function
+    case WK_POT: return launch_typed<T, D, WK_POT>(a, st);
+    case WK_POT_FLUSH: return launch_typed<T, D, WK_POT_FLUSH>(a, st);
+    case WK_KH: return launch_typed<T, D, WK_KH>(a, st);
+    case WK_KH_FLUSH: return launch_typed<T, D, WK_KH_FLUSH>(a, st);
+    case WK_KI: return launch_typed<T, D, WK_KI>(a, st);
+    case WK_KI_FLUSH: return launch_typed<T, D, WK_KI_FLUSH>(a, st);
+    case WK_TRUNC: return launch_typed<T, D, WK_TRUNC>(a, st);
+    case WK_UNIF: return launch_typed<T, D, WK_UNIF>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int d, int wk, hipStream_t st) {
+  if (a.bf16) {
+    if (d == 64) return launch_kind<__bf16, 64>(a, wk, st);
+    if (d == 128) return launch_kind<__bf16, 128>(a, wk, st);
+  } else {
+    if (d == 64) return launch_kind<float, 64>(a, wk, st);
+    if (d == 128) return launch_kind<float, 128>(a, wk, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qsa

@@ -48,9 +48,22 @@ struct FwdArgs {
   int total_blocks;    // B * H * n_qtiles
 };
 
+// Backward: the forward's arguments (shapes, kind, scale, calibration; q/k/v; o unused) plus
+// the output gradient and the three input gradients (float32).
+struct BwdArgs {
+  FwdArgs f;
+  const void* dout;   // dO [B,H,N,d], the dtype of Q
+  float* dq;          // [B,H,N,d]; also holds per-row constants between the launches
+  float* dk;          // [B,Hkv,N,d]
+  float* dv;          // [B,Hkv,N,d]
+  int mode;           // 0 straight-through, 1 exact, 2 exact with the extrema detached
+  int bf16;           // inputs are bf16 (else float32)
+};
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_bf16(const FwdArgs& a, int d, int wk, hipStream_t s);
 hipError_t launch_fp8(const FwdArgs& a, int d, int wk, hipStream_t s);
 hipError_t launch_f32(const FwdArgs& a, int d, int wk, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int d, int wk, hipStream_t s);
 
 }  // namespace qsa

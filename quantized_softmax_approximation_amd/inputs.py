@@ -115,6 +115,19 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
     raise ValueError(f"unknown dtype {wl.dtype!r}")
 
 
+def make_dout(wl: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """Output gradient dO for workload ``wl``: ``standard_normal`` float32 of shape
+    [B,H,N,d] from ``PCG64(seed)`` (default: the workload's seed + 1), cast to the
+    stored dtype (float32 or bf16)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 1 if seed is None else seed))
+    g = torch.from_numpy(_draw(rng, (wl.B, wl.H, wl.N, wl.d), 1.0))
+    if wl.dtype == "f32":
+        return g
+    if wl.dtype == "bf16":
+        return g.to(torch.bfloat16)
+    raise ValueError(f"the backward takes f32 or bf16, not {wl.dtype!r}")
+
+
 def custom(name="custom", *, B=1, H=1, Hkv=None, N=64, d=64, dtype="bf16", causal=False,
            sigma_qk=1.0, seed=7, sink=False) -> Workload:
     """A workload with explicit sizes (tests: ragged tails, edge cases)."""

@@ -30,8 +30,8 @@ def v(**kw):
 def test_every_declared_symbol_is_exported():
     src = open(HEADER).read()
     names = re.findall(r"^\s*(?:int|const char\*)\s+(qsa_\w+)\s*\(", src, flags=re.M)
-    assert set(names) == {"qsa_attn_fwd", "qsa_attn_fwd_ex", "qsa_attn_validate", "qsa_status_string",
-                          "qsa_last_error", "qsa_version"}
+    assert set(names) == {"qsa_attn_fwd", "qsa_attn_fwd_ex", "qsa_attn_bwd", "qsa_attn_validate",
+                          "qsa_status_string", "qsa_last_error", "qsa_version"}
     L = ctypes.CDLL(qsa.lib_path(), mode=os.RTLD_NOW | os.RTLD_LOCAL)  # every symbol resolves at load
     for n in names:
         assert hasattr(L, n), n
@@ -50,7 +50,11 @@ def test_header_constants_match_binding():
     for name, val in [("QSA_EXACT", qsa.EXACT), ("QSA_KINT", qsa.KINT), ("QSA_POT", qsa.POT),
                       ("QSA_EXACT_ANCHORED", qsa.EXACT_ANCHORED), ("QSA_TRUNC", qsa.TRUNC),
                       ("QSA_UNIFORM", qsa.UNIFORM), ("QSA_DT_F32", qsa.DT_F32),
-                      ("QSA_DT_BF16", qsa.DT_BF16), ("QSA_DT_FP8_E4M3", qsa.DT_FP8_E4M3)]:
+                      ("QSA_DT_BF16", qsa.DT_BF16), ("QSA_DT_FP8_E4M3", qsa.DT_FP8_E4M3),
+                      ("QSA_GRAD_STE_POST", qsa.GRADS["ste_post"]), ("QSA_GRAD_EXACT", qsa.GRADS["exact"]),
+                      ("QSA_GRAD_EXACT_DETACHED", qsa.GRADS["exact_detached"]),
+                      ("QSA_GRAD_STE_PRE", qsa.GRADS["ste_pre"]),
+                      ("QSA_GRAD_STE_PRE_DETACHED", qsa.GRADS["ste_pre_detached"])]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == val, name
     for name, val in [("QSA_F_INTERP", qsa.F_INTERP), ("QSA_F_WINDOW", qsa.F_WINDOW), ("QSA_F_FLUSH", qsa.F_FLUSH)]:
@@ -150,3 +154,38 @@ def test_binding_rejects_bad_tensors_on_host():
         qsa.attn_fwd_ex(q, q[:, :, :4], q)            # shape mismatch
     with pytest.raises(ValueError):
         qsa.attn_fwd_ex(q, q.double(), q)             # dtype mismatch
+
+
+def _bwd(ptrs=(1, 1, 1, 1, 1, 1, 1), grad=0, scale=0.0, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return qsa.lib().qsa_attn_bwd(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"], a["variant"],
+                                  a["k_levels"], a["window"], a["dtype"], grad, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), qsa.ERR_SHAPE), (dict(H=3), qsa.ERR_SHAPE), (dict(d=96), qsa.ERR_UNSUPPORTED),
+    (dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_UNSUPPORTED), (dict(grad=-1), qsa.ERR_PARAM),
+    (dict(grad=5), qsa.ERR_PARAM), (dict(scale=-1.0), qsa.ERR_PARAM), (dict(scale=math.nan), qsa.ERR_PARAM),
+    (dict(variant=qsa.KINT, k_levels=0), qsa.ERR_PARAM), (dict(variant=qsa.TRUNC, window=0.0), qsa.ERR_PARAM),
+])
+def test_backward_validation_before_any_hip_call(kw, status):
+    assert _bwd(**kw) == status
+    assert qsa.last_error() != ""
+
+
+def test_backward_null_pointers_rejected():
+    for i in range(7):
+        ptrs = [1] * 7
+        ptrs[i] = None
+        assert _bwd(ptrs=tuple(ptrs)) == qsa.ERR_NULL_PTR
+    assert _bwd(ptrs=(None,) * 7, B=0) == qsa.ERR_SHAPE      # validation first
+
+
+def test_backward_binding_rejects_bad_tensors_on_host():
+    import torch
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        qsa.attn_bwd(q, q, q, q)                      # CPU tensors
+    with pytest.raises(ValueError):
+        qsa.attn_bwd(q, q, q, q, grad="nope")         # unknown mode
