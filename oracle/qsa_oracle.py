@@ -29,6 +29,17 @@ with three kinds of weight function w(s) replacing exp(s - m):
   "Row max -> Power-of-two weights"): a coarse logarithmic weight anchored at
   the row maximum.  With y = (m_i - s) * log2(e), e = rint(y) clipped to the
   stated level count L, w = 2**-e.
+* ``pot_running`` -- a single-pass form of the power-of-two weights with no
+  row-maximum pre-pass (the Rowmax-PoT page names a max-anchored variant built
+  into FlashAttention-4 without saying how it obtains the maximum).  Keys are
+  taken in tiles of ``tile`` consecutive keys (64, the kernels' key tile); after
+  each tile the row's anchor becomes A = ceil(running max of s * log2(e)), an
+  integer, so that a key's exponent e = rint(A - s log2(e)), clipped to L-1 (or
+  flushed beyond it) against the anchor in force when its tile was weighed,
+  stays exact when a later rise of the anchor by an integer dA rescales every
+  earlier weight by 2**-dA.  Its final weight is 2**-(e + A_final - A_tile).
+  Without the clip this is 2**rint(s log2 e) normalised: a power-of-two grid
+  fixed at integer log2 values instead of aligned with the row maximum.
 * ``trunc`` and ``uniform`` -- the two operators of the sensitivity study on
   the same "Approximating Softmax" page (abstract): the softmax support can be
   cut to the scores close to the row maximum with little loss, while giving
@@ -67,6 +78,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 LOG2E = 1.0 / math.log(2.0)
+ANCHOR_TILE = 64          # keys per anchor update of pot_running (the kernels' key tile)
 IDX_FLUSHED = 254
 IDX_MASKED = 255
 
@@ -107,7 +119,7 @@ def decode_e4m3fn(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def _check_kind(kind, levels, window, interp, flush):
-    if kind not in ("exact", "kint", "pot", "trunc", "uniform"):
+    if kind not in ("exact", "kint", "pot", "pot_running", "trunc", "uniform"):
         raise ValueError(f"unknown kind {kind!r}")
     if kind in ("trunc", "uniform"):
         if window is None or not (window > 0 and math.isfinite(window)):
@@ -119,6 +131,9 @@ def _check_kind(kind, levels, window, interp, flush):
         raise ValueError("kint needs levels = K >= 1 intervals")
     if kind == "pot" and not (isinstance(levels, int) and levels >= 1):
         raise ValueError("pot needs levels = L >= 1")
+    if kind == "pot_running" and not (isinstance(levels, int) and levels >= 2):
+        # the row maximum sits at e = 0 or 1 below the rounded-up anchor: L >= 2 keeps it
+        raise ValueError("pot_running needs levels = L >= 2")
     if window is not None and not (window > 0 and math.isfinite(window)):
         raise ValueError("window must be finite and > 0")
     if interp and kind != "kint":
@@ -131,13 +146,16 @@ def _check_kind(kind, levels, window, interp, flush):
 
 def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Optional[int] = None,
                 window: Optional[float] = None, interp: bool = False, flush: bool = False,
-                extrema: Optional[tuple] = None):
+                extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE):
     """Weights for a block of score rows.
 
     S: (R, N) float64 scaled scores; visible: (R, N) bool, at least one True
     per row.  Returns dict with w (R,N), idx (R,N) uint8, y (R,N) grid
-    coordinate (nan where masked; for exact kinds y = m - s), m, lo, delta (R,)
-    and the table T (R, K+1) for kint.  ``extrema`` = (m, mn), each (R,),
+    coordinate (nan where masked; for exact kinds y = m - s; pot_running: the
+    rounded A_tile - s log2 e), m, lo, delta (R,) and the table T (R, K+1) for
+    kint; pot_running also gives the final anchor A (R,) in log2 units.  The
+    columns of S are the keys in order (pot_running visits them in tiles of
+    ``tile``).  ``extrema`` = (m, mn), each (R,),
     replaces the row maximum and minimum (the forward with the calibration held
     fixed, whose derivative is the detached gradient).
     """
@@ -171,6 +189,28 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
         idx[visible & ~kept] = IDX_FLUSHED
         y = np.where(visible, (m[:, None] - S) / window, np.nan)   # the support edge is y = 1
         out.update(w=w, idx=idx, y=y, lo=m - window, delta=np.full(R, float(window)))
+        return out
+
+    if kind == "pot_running":
+        L = levels
+        t = np.where(visible, S * LOG2E, -np.inf)             # scores in log2 units
+        nt = (N + tile - 1) // tile
+        tmax = np.stack([t[:, c * tile:(c + 1) * tile].max(axis=1) for c in range(nt)], axis=1)
+        A = np.ceil(np.maximum.accumulate(tmax, axis=1))      # anchor after each tile (-inf before any key)
+        Aj = np.repeat(A, tile, axis=1)[:, :N]                # the anchor a key's tile was weighed with
+        Afin = A[:, -1]
+        y = np.where(visible, Aj - np.where(visible, t, 0.0), np.nan)
+        ex = np.rint(np.where(visible, y, 0.0))               # exponent against the tile's anchor
+        if flush:
+            keep = visible & (ex <= L - 1)
+        else:
+            ex = np.minimum(ex, L - 1)
+            keep = visible
+        shift = np.where(visible, Afin[:, None] - Aj, 0.0)    # later rises of the anchor
+        w = np.where(keep, np.exp2(-(np.where(keep, ex, 0.0) + shift)), 0.0)
+        idx[keep] = ex[keep].astype(np.uint8)
+        idx[visible & ~keep] = IDX_FLUSHED
+        out.update(w=w, idx=idx, y=y, lo=mn, delta=np.full(R, 1.0 / LOG2E), A=Afin)
         return out
 
     if kind == "pot":
@@ -240,7 +280,7 @@ def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Seq
               causal: bool = False, kind: str = "exact", levels: Optional[int] = None,
               window: Optional[float] = None, interp: bool = False, flush: bool = False,
               scale: Optional[float] = None, detail: bool = False, chunk: int = 512,
-              extrema: Optional[tuple] = None):
+              extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE):
     """One (batch, head) pair: qh (N, d), kh/vh (N, d) float64.
 
     ``rows`` selects query rows (default: all).  Returns dict with O (R, d),
@@ -258,13 +298,15 @@ def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Seq
         visible = (cols[None, :] <= r[:, None]) if causal else np.ones((len(r), N), dtype=bool)
         ext = None if extrema is None else (np.asarray(extrema[0])[r], np.asarray(extrema[1])[r])
         rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush,
-                         extrema=ext)
+                         extrema=ext, tile=tile)
         w = rw["w"]
         l = w.sum(axis=1)                                  # row sum of the approximate weights
         O = (w @ vh) / l[:, None]                          # normalise, then P.V
         piece = {"O": O, "m": rw["m"], "lo": rw["lo"], "l": l}
         if detail:
             piece.update(w=w, idx=rw["idx"], y=rw["y"], delta=rw["delta"])
+            if "A" in rw:
+                piece["A"] = rw["A"]
         for key, val in piece.items():
             parts.setdefault(key, []).append(val)
     return {key: np.concatenate(val, axis=0) for key, val in parts.items()}
@@ -381,6 +423,8 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
     ``extrema`` (detached modes only) = (m, mn) per row, as in row_weights."""
     if grad not in GRADS:
         raise ValueError(f"unknown gradient mode {grad!r}")
+    if kind == "pot_running":
+        raise ValueError("the backward covers the max-anchored kinds, not pot_running")
     detached = grad.endswith("_detached")
     if extrema is not None and not detached:
         raise ValueError("fixed extrema go with a detached gradient")

@@ -16,7 +16,11 @@ Definitions followed (readings as in the vectorised oracle):
   row maximum);
   support truncation and uniform weighting -- the same abstract's sensitivity
   study (keep only the scores within W of the row maximum, with their exact
-  weights or with equal weights).
+  weights or with equal weights);
+  single-pass power-of-two weights (``pot_running``) -- simulated here as a
+  pass over the keys that keeps a running integer anchor and rescales the
+  weights already formed whenever the anchor rises, instead of the vectorised
+  oracle's closed form.
 """
 from __future__ import annotations
 
@@ -34,11 +38,42 @@ def _round_half_even(x: float) -> int:
     return f if f % 2 == 0 else f + 1
 
 
-def weight_row(scores, visible, kind, levels=None, window=None, interp=False, flush=False, exact_pot=False):
+def _running_pot_row(scores, visible, L, flush, tile, exact):
+    """Single-pass power-of-two weights: tiles of ``tile`` keys in order; after a
+    tile's maximum is seen the anchor A = ceil(max so far of s log2 e) may rise,
+    and every weight formed before is multiplied by 2**-(rise)."""
+    inv_ln2 = 1.0 / math.log(2.0)
+    one = Fraction(1) if exact else 1.0
+    w = [0 * one] * len(scores)
+    A = None
+    for start in range(0, len(scores), tile):
+        keys = [j for j in range(start, min(start + tile, len(scores))) if visible[j]]
+        if not keys:
+            continue
+        top = math.ceil(max(scores[j] * inv_ln2 for j in keys))
+        if A is not None and top > A:
+            for j in range(start):
+                w[j] = w[j] / (2 ** (top - A))
+        if A is None or top > A:
+            A = top
+        for j in keys:
+            e = _round_half_even(A - scores[j] * inv_ln2)
+            if e > L - 1:
+                if flush:
+                    continue
+                e = L - 1
+            w[j] = one / (2 ** e)
+    return w
+
+
+def weight_row(scores, visible, kind, levels=None, window=None, interp=False, flush=False, exact_pot=False,
+               tile=64):
     """Weights of one row of scaled scores (list of float) -> list of weights.
 
     Masked keys get weight 0.  With ``exact_pot`` PoT weights are Fractions.
     """
+    if kind == "pot_running":
+        return _running_pot_row(scores, visible, levels, flush, tile, exact_pot)
     vis = [s for s, ok in zip(scores, visible) if ok]
     m = max(vis)
     mn = min(vis)
@@ -100,7 +135,7 @@ def weight_row(scores, visible, kind, levels=None, window=None, interp=False, fl
 
 
 def attention(q, k, v, causal=False, kind="exact", levels=None, window=None, interp=False, flush=False,
-              scale=None, exact_pot=False):
+              scale=None, exact_pot=False, tile=64):
     """One head: q, k, v lists of rows (lists of float).  Returns O rows.
 
     With ``exact_pot`` (kind "pot"), scores are still floats but the weights
@@ -119,7 +154,8 @@ def attention(q, k, v, causal=False, kind="exact", levels=None, window=None, int
                 acc += q[i][c] * k[j][c]
             scores.append(sc * acc)
         visible = [(j <= i) if causal else True for j in range(nk)]
-        w = weight_row(scores, visible, kind, levels, window, interp, flush, exact_pot and kind == "pot")
+        w = weight_row(scores, visible, kind, levels, window, interp, flush,
+                       exact_pot and kind in ("pot", "pot_running"), tile)
         total = sum(w)
         row = []
         for c in range(len(v[0])):

@@ -45,6 +45,13 @@ MUTATIONS = {
     "support_sign": ("kept = visible & (m[:, None] - S <= window)", "kept = visible & (S - m[:, None] <= window)"),
     "uniform_takes_exact_weights": ("w = kept.astype(np.float64)",
                                     "w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)"),
+    "running_anchor_not_running": ("A = np.ceil(np.maximum.accumulate(tmax, axis=1))", "A = np.ceil(tmax)"),
+    "running_anchor_floor": ("A = np.ceil(np.maximum.accumulate(tmax, axis=1))",
+                             "A = np.floor(np.maximum.accumulate(tmax, axis=1))"),
+    "running_rescale_sign": ("shift = np.where(visible, Afin[:, None] - Aj, 0.0)",
+                             "shift = np.where(visible, Aj - Afin[:, None], 0.0)"),
+    "running_no_clip": ("ex = np.minimum(ex, L - 1)", "ex = ex"),
+    "running_flush_threshold": ("keep = visible & (ex <= L - 1)", "keep = visible & (ex <= L)"),
     "trunc_takes_unit_weights": ("w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)\n        else:",
                                  "w = kept.astype(np.float64)\n        else:"),
 }
@@ -90,6 +97,18 @@ def _checks(o):
                     r = o.attn_fwd(qq, kk, vv, causal=causal, **var)
                     rs = scalar.attention(qq[0, 0].tolist(), kk[0, 0].tolist(), vv[0, 0].tolist(), causal=causal, **var)
                     np.testing.assert_allclose(r["O"][0, 0], np.array(rs), atol=1e-12)
+        # single-pass power-of-two weights: the stateful scalar simulation, several tiles per row
+        for var in (dict(levels=2), dict(levels=3), dict(levels=3, flush=True), dict(levels=2, flush=True)):
+            for causal in (False, True):
+                for tile in (2, 3):
+                    qq = rng.standard_normal((1, 1, 9, 4)) * 2.5
+                    kk = rng.standard_normal((1, 1, 9, 4)) * 2.5
+                    vv = rng.standard_normal((1, 1, 9, 4))
+                    r = o.head_rows(qq[0, 0], kk[0, 0], vv[0, 0], causal=causal, kind="pot_running", tile=tile,
+                                    **var)
+                    rs = scalar.attention(qq[0, 0].tolist(), kk[0, 0].tolist(), vv[0, 0].tolist(), causal=causal,
+                                          kind="pot_running", tile=tile, **var)
+                    np.testing.assert_allclose(r["O"], np.array(rs), atol=1e-12)
         # sensitivity operators: the inclusive support edge on integer scores, then the closed forms
         qe = np.array([[[[1.0, 0.0]]]])
         ke = np.array([[[[5.0, 0.0], [3.0, 0.0], [2.0, 0.0], [4.0, 0.0]]]])
