@@ -49,8 +49,9 @@ def pairs(B, H, N, causal):
 
 def mfma_flops_per_pair(kind, d):
     """MFMA work the algorithm needs per visible pair: QK^T and PV (2d each),
-    plus one more QK^T for the row-extrema pre-pass of anchored kinds."""
-    return 4 * d if kind == "exact" else 6 * d
+    plus one more QK^T for the row-extrema pre-pass of anchored kinds (the online exact
+    control and the single-pass PoT have none)."""
+    return 4 * d if kind in ("exact", "pot_running") else 6 * d
 
 
 def src_hash():
@@ -257,11 +258,10 @@ def energy_run(args):
 BWD_FLOPS_PER_PAIR_D = 10   # algorithmic backward: S recompute, dP, dV, dK, dQ (2 d flops each per pair)
 
 
-def bwd_executed_flops_per_pair(d, attached):
+def bwd_executed_flops_per_pair(d):
     """fp32 FMA work the three backward launches execute per visible pair (2 flops per FMA):
-    rows 2 passes of (S, dP) plus one more when the extrema are attached; keys S, dP, dV, dK;
-    dQ S, dP, dQ."""
-    return 2 * d * ((6 if attached else 4) + 4 + 3)
+    rows S twice and dP once; keys S, dP, dV, dK; dQ S, dP, dQ."""
+    return 2 * d * (3 + 4 + 3)
 
 
 def cpu_baseline_bwd(wl, x, do, var, grad, budget_s):
@@ -308,7 +308,7 @@ def backward_run(args):
     ms, wall = time_loop(lambda: fn(*head), args.steps, args.warmup)
     credited = BWD_FLOPS_PER_PAIR_D * d * P
     tflops = credited / (ms * 1e-3) / 1e12
-    executed = bwd_executed_flops_per_pair(d, True) * P
+    executed = bwd_executed_flops_per_pair(d) * P
     rec = {
         "metric": "attention bwd TFLOP/s (credited 10 d flops per visible pair)", "value": round(tflops, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -319,7 +319,7 @@ def backward_run(args):
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_TFLOPS["f32"], 4), "traffic": None,
                      "flops_per_launch": credited, "flops_per_pair": BWD_FLOPS_PER_PAIR_D * d,
-                     "executed_flops_per_pair": bwd_executed_flops_per_pair(d, True),
+                     "executed_flops_per_pair": bwd_executed_flops_per_pair(d),
                      "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 3),
                      "note": "the three launches of one call timed together (HIP events); fp32 vector FMA peak"},
     }
@@ -370,7 +370,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_8k", choices=sorted(qin.WORKLOADS))
     ap.add_argument("--dtype", default=None, choices=["fp8", "bf16", "f32"])
-    ap.add_argument("--kind", default="pot", choices=["pot", "exact", "exact_anchored", "kint", "trunc", "uniform"])
+    ap.add_argument("--kind", default="pot",
+                    choices=["pot", "exact", "exact_anchored", "kint", "trunc", "uniform", "pot_running"])
     ap.add_argument("--levels", type=int, default=16)
     ap.add_argument("--window", type=float, default=None)
     ap.add_argument("--interp", action="store_true")
@@ -417,7 +418,7 @@ def main(argv=None):
     odt = torch.float32 if x.q.dtype == torch.float32 else torch.bfloat16
     out = torch.empty((B, H, N, d), dtype=odt, device="cuda")
     var = {"kind": args.kind}
-    if args.kind in ("pot", "kint"):
+    if args.kind in ("pot", "kint", "pot_running"):
         var["levels"] = args.levels
     if args.window is not None:
         var["window"] = args.window
@@ -466,6 +467,7 @@ def main(argv=None):
         table = {}
         for vname, vv in [("exact_online", {"kind": "exact"}), ("exact_anchored", {"kind": "exact_anchored"}),
                           ("pot16", {"kind": "pot", "levels": 16}), ("pot8", {"kind": "pot", "levels": 8}),
+                          ("pot16_single_pass", {"kind": "pot_running", "levels": 16}),
                           ("kint16_window8_hard", {"kind": "kint", "levels": 16, "window": 8.0}),
                           ("kint16_minmax_hard", {"kind": "kint", "levels": 16}),
                           ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True}),
@@ -488,6 +490,9 @@ def main(argv=None):
                 "disjoint_p10_p90": p["p90_ms"] < e["p10_ms"]}
             eo = table[f"exact_online:{c}"]
             rec.setdefault("pot_vs_exact_online", {})[c] = {"speedup": round(eo["median_ms"] / p["median_ms"], 4)}
+            r = table[f"pot16_single_pass:{c}"]
+            rec.setdefault("single_pass_pot_vs_pot16", {})[c] = {"speedup": round(p["median_ms"] / r["median_ms"], 4),
+                                                                "vs_exact_online": round(eo["median_ms"] / r["median_ms"], 4)}
         rec["b200_context"] = {"fp8_8k_causal_speedup_pct": 12.4, "fp8_8k_noncausal_speedup_pct": 25.8,
                                "note": "the pages' B200 FlashAttention-4 figures; context, not a target"}
 

@@ -102,11 +102,23 @@ typedef enum {
  *                     keys with s >= m - window, 0 for the others, so each row
  *                     of O is the mean of the kept rows of V (the same study:
  *                     equal weights on the kept positions hurt).
+ * QSA_POT_RUNNING     single-pass power-of-two weights with no row-maximum
+ *                     pre-pass (the Rowmax-PoT page names a max-anchored
+ *                     variant inside FlashAttention-4 without saying how the
+ *                     maximum is found; this form is the library's own).  Keys
+ *                     are visited in tiles of 64; after each tile the row's
+ *                     anchor becomes A = ceil(running max of s log2 e), an
+ *                     integer; a key's exponent e = rint(A - s log2 e) is
+ *                     clipped to L-1 (or flushed) against the anchor of its
+ *                     tile, and every rise of A by dA rescales the weights
+ *                     formed before by 2^-dA exactly.  Without the clip the
+ *                     weights are 2^rint(s log2 e), normalised.  L = k_levels
+ *                     >= 2 (the row maximum lands on e = 0 or 1).
  *
  * QSA_F_INTERP        K-interval only: linear interpolation.
  * QSA_F_WINDOW        K-interval only: fixed-window calibration [m - window, m].
- * QSA_F_FLUSH         K-interval (window) and PoT: scores outside the grid
- *                     (K-interval: s < m - window; PoT: e >= L) get weight 0
+ * QSA_F_FLUSH         K-interval (window) and both PoT kinds: scores outside the
+ *                     grid (K-interval: s < m - window; PoT: e >= L) get weight 0
  *                     instead of the last grid value.  On a min-max K-interval
  *                     grid every visible score lies inside, so the flag is
  *                     accepted and changes nothing.
@@ -120,6 +132,7 @@ enum {
   QSA_EXACT_ANCHORED = 3,
   QSA_TRUNC = 4,
   QSA_UNIFORM = 5,
+  QSA_POT_RUNNING = 6,
   QSA_BASE_MASK = 0x0F,
   QSA_F_INTERP = 1 << 4,
   QSA_F_WINDOW = 1 << 5,
@@ -134,7 +147,8 @@ enum {
  * Limits checked by validation:
  *   1 <= B, H, Hkv;  H % Hkv == 0;  1 <= N <= 2^20;  d in {64, 128};
  *   B*H*N*d < 2^31 and B*Hkv*N*d < 2^31 (element offsets are 32-bit);
- *   QSA_KINT: 1 <= k_levels <= 64;  QSA_POT: 1 <= k_levels <= 64
+ *   QSA_KINT: 1 <= k_levels <= 64;  QSA_POT: 1 <= k_levels <= 64;
+ *   QSA_POT_RUNNING: 2 <= k_levels <= 64
  *   (fp8: k_levels <= 16, so the power-of-two weights stay exact in the
  *   8-bit operand of the PV product);
  *   QSA_F_WINDOW, QSA_TRUNC, QSA_UNIFORM: window finite and > 0;
@@ -170,15 +184,18 @@ typedef struct {
   float q_descale;             /* fp8 per-tensor descales: stored value * descale = real */
   float k_descale;             /*   value; 0 -> 1.  Must be 1 or 0 for non-fp8 dtypes.   */
   float v_descale;
-  float* row_max;              /* [B,H,N] float32: m_i (the anchor).                     */
+  float* row_max;              /* [B,H,N] float32: m_i (the anchor); QSA_POT_RUNNING:    */
+                               /*   the final anchor A_i ln 2 (>= m_i, A_i an integer).   */
   float* row_lo;               /* [B,H,N] float32: K-interval: the calibrated lower end  */
                                /*   lo_i; QSA_TRUNC / QSA_UNIFORM: the support edge      */
                                /*   m_i - window; other anchored kinds: the visible row  */
                                /*   minimum.                                             */
-                               /*   Not available for QSA_EXACT (must be NULL).          */
+                               /*   Not available for QSA_EXACT and QSA_POT_RUNNING      */
+                               /*   (must be NULL).                                      */
   float* row_sum;              /* [B,H,N] float32: l_i = sum_j w_ij of the weights that  */
                                /*   entered the PV product (QSA_EXACT: relative to the   */
-                               /*   final running maximum).                              */
+                               /*   final running maximum; QSA_POT_RUNNING: to the final */
+                               /*   anchor).                                             */
   unsigned char* grid_idx;     /* [B,H,idx_rows,N] u8: per element the grid index l (K-  */
                                /*   interval; interpolation: floor(y) clipped to K) or   */
                                /*   the exponent e (PoT); 0 for exact kinds and for the  */

@@ -19,13 +19,14 @@ from typing import Optional
 import torch
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_validate", "GRADS", "variant_code", "status_string", "last_error",
-           "version", "lib", "lib_path", "QSAError", "EXACT", "KINT", "POT", "EXACT_ANCHORED", "TRUNC", "UNIFORM", "F_INTERP",
+           "version", "lib", "lib_path", "QSAError", "EXACT", "KINT", "POT", "EXACT_ANCHORED", "TRUNC", "UNIFORM",
+           "POT_RUNNING", "F_INTERP",
            "F_WINDOW", "F_FLUSH", "DT_F32", "DT_BF16", "DT_FP8_E4M3", "IDX_FLUSHED", "IDX_MASKED"]
 
 # ABI constants (include/qsa.h)
 OK, ERR_NULL_PTR, ERR_SHAPE, ERR_PARAM, ERR_UNSUPPORTED, ERR_HIP = range(6)
 DT_F32, DT_BF16, DT_FP8_E4M3 = 0, 1, 2
-EXACT, KINT, POT, EXACT_ANCHORED, TRUNC, UNIFORM = 0, 1, 2, 3, 4, 5
+EXACT, KINT, POT, EXACT_ANCHORED, TRUNC, UNIFORM, POT_RUNNING = 0, 1, 2, 3, 4, 5, 6
 F_INTERP, F_WINDOW, F_FLUSH = 1 << 4, 1 << 5, 1 << 6
 IDX_FLUSHED, IDX_MASKED = 254, 255
 GRAD_STE_POST, GRAD_EXACT, GRAD_EXACT_DETACHED, GRAD_STE_PRE, GRAD_STE_PRE_DETACHED = range(5)
@@ -94,10 +95,10 @@ def version() -> int:
 
 def variant_code(kind: str = "exact", *, interp: bool = False, window: Optional[float] = None,
                  flush: bool = False) -> int:
-    """Variant bits for kind in {"exact", "exact_anchored", "kint", "pot", "trunc", "uniform"} plus
-    flags.  For "trunc" and "uniform" the window is the support width W, not a flag."""
+    """Variant bits for kind in {"exact", "exact_anchored", "kint", "pot", "pot_running", "trunc",
+    "uniform"} plus flags.  For "trunc" and "uniform" the window is the support width W, not a flag."""
     base = {"exact": EXACT, "kint": KINT, "pot": POT, "exact_anchored": EXACT_ANCHORED, "trunc": TRUNC,
-            "uniform": UNIFORM}[kind]
+            "uniform": UNIFORM, "pot_running": POT_RUNNING}[kind]
     if base in (TRUNC, UNIFORM):
         return base | (F_INTERP if interp else 0) | (F_FLUSH if flush else 0)
     return base | (F_INTERP if interp else 0) | (F_WINDOW if window is not None else 0) | (F_FLUSH if flush else 0)

@@ -43,7 +43,7 @@ int validate(int B, int H, int Hkv, int N, int d, int causal, int variant, int k
   const int flags = variant & ~QSA_BASE_MASK;
   if (flags & ~(QSA_F_INTERP | QSA_F_WINDOW | QSA_F_FLUSH))
     return fail(QSA_ERR_PARAM, "unknown variant flag bits 0x%x", flags);
-  if (base > QSA_UNIFORM) return fail(QSA_ERR_PARAM, "unknown variant kind %d", base);
+  if (base > QSA_POT_RUNNING) return fail(QSA_ERR_PARAM, "unknown variant kind %d", base);
   if (base == QSA_TRUNC || base == QSA_UNIFORM) {
     if (flags) return fail(QSA_ERR_PARAM, "support truncation and uniform weighting take no flags");
     if (!(std::isfinite(window) && window > 0.0f))
@@ -56,6 +56,12 @@ int validate(int B, int H, int Hkv, int N, int d, int causal, int variant, int k
     return fail(QSA_ERR_PARAM, "flush applies to K-interval and PoT");
   if (base == QSA_KINT && (k_levels < 1 || k_levels > 64))
     return fail(QSA_ERR_PARAM, "K-interval needs 1 <= K <= 64 (got %d)", k_levels);
+  if (base == QSA_POT_RUNNING) {
+    if (k_levels < 2 || k_levels > 64)
+      return fail(QSA_ERR_PARAM, "single-pass PoT needs 2 <= L <= 64 (got %d)", k_levels);
+    if (dtype == QSA_DT_FP8_E4M3 && k_levels > 16)
+      return fail(QSA_ERR_PARAM, "PoT on fp8 needs L <= 16 (got %d)", k_levels);
+  }
   if (base == QSA_POT) {
     if (k_levels < 1 || k_levels > 64) return fail(QSA_ERR_PARAM, "PoT needs 1 <= L <= 64 (got %d)", k_levels);
     if (dtype == QSA_DT_FP8_E4M3 && k_levels > 16)
@@ -78,6 +84,7 @@ int weight_kind(int variant) {
     case QSA_EXACT: return qsa::WK_EXACT;
     case QSA_EXACT_ANCHORED: return qsa::WK_EXACT_ANCH;
     case QSA_POT: return flush ? qsa::WK_POT_FLUSH : qsa::WK_POT;
+    case QSA_POT_RUNNING: return flush ? qsa::WK_POTR_FLUSH : qsa::WK_POTR;
     case QSA_TRUNC: return qsa::WK_TRUNC;
     case QSA_UNIFORM: return qsa::WK_UNIF;
     default: return interp ? (flush ? qsa::WK_KI_FLUSH : qsa::WK_KI) : (flush ? qsa::WK_KH_FLUSH : qsa::WK_KH);
@@ -113,8 +120,8 @@ int qsa_attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, int B,
   if (!descale_ok(x.q_descale, fp8) || !descale_ok(x.k_descale, fp8) || !descale_ok(x.v_descale, fp8))
     return fail(QSA_ERR_PARAM, "descales must be finite and > 0 for fp8, and 0 or 1 otherwise");
   const int base = variant & QSA_BASE_MASK;
-  if (x.row_lo && base == QSA_EXACT)
-    return fail(QSA_ERR_PARAM, "row_lo needs an anchored kind (the online exact kind has no pre-pass)");
+  if (x.row_lo && (base == QSA_EXACT || base == QSA_POT_RUNNING))
+    return fail(QSA_ERR_PARAM, "row_lo needs a kind with the row-extrema pre-pass");
   if (x.grid_idx) {
     if (x.idx_row0 < 0 || x.idx_rows < 1 || (int64_t)x.idx_row0 + x.idx_rows > N)
       return fail(QSA_ERR_SHAPE, "grid_idx rows [%d, %d+%d) outside [0, N=%d)", x.idx_row0, x.idx_row0,
@@ -173,6 +180,8 @@ int qsa_attn_bwd(const void* Q, const void* K, const void* V, const void* dO, fl
   int st = validate(B, H, Hkv, N, d, causal, variant, k_levels, window, dtype);
   if (st != QSA_OK) return st;
   if (dtype == QSA_DT_FP8_E4M3) return fail(QSA_ERR_UNSUPPORTED, "the backward takes float32 or bfloat16 inputs");
+  if ((variant & QSA_BASE_MASK) == QSA_POT_RUNNING)
+    return fail(QSA_ERR_UNSUPPORTED, "the backward covers the kinds anchored at the row maximum");
   if (grad < QSA_GRAD_STE_POST || grad > QSA_GRAD_STE_PRE_DETACHED)
     return fail(QSA_ERR_PARAM, "unknown gradient mode %d", grad);
   if (!(std::isfinite(scale) && scale >= 0.0f))

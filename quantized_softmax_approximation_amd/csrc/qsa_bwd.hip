@@ -23,8 +23,9 @@
 // key (lane u of a quad holds dimensions u, u+4, ..., so quads read LDS without bank
 // conflicts), fp32 FMAs, 64-row or 64-key tiles staged in LDS.  Three launches on the caller's
 // stream:
-//   bwd_rows  per query row: the extrema and their keys, l, D and (attached modes) the
-//             gradients of m and lo, parked in the first 8 floats of the row's dQ;
+//   bwd_rows  per query row, two passes over its keys: the extrema and their keys; then l, D
+//             and (attached modes) the gradients of m and lo, parked in the first 8 floats
+//             of the row's dQ;
 //   bwd_keys  per key: dK and dV, summed over the query heads that read the key's KV head;
 //   bwd_dq    per query row: dQ (it reads its parked constants, then overwrites the row).
 // Every launch computes scores with the same operation order, so the three agree exactly on
@@ -183,8 +184,12 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   const float dsc = wk_kint(WK) ? grid_step(f, M, MN) : 1.0f;
   const bool minmax = wk_kint(WK) && !f.window_calib;
 
-  // l and D = sum_j P_ij dP_ij (= dO_i . O_i)
-  float l = 0.0f, wdp = 0.0f;
+  // l, D = sum_j P_ij dP_ij (= dO_i . O_i) and, with the extrema attached, the gradients of m
+  // and lo: dm = sum_j (dP_ij - D) cm_ij / l is linear in D, so one pass gathers
+  // sum dP cm and sum cm (likewise for lo) before D is known
+  const bool calib = g_attached(a.mode) &&
+                     (WK == WK_TRUNC || wk_kint(WK) || ((WK == WK_POT || WK == WK_POT_FLUSH) && g_ste(a.mode)));
+  float l = 0.0f, wdp = 0.0f, pm = 0.0f, sm = 0.0f, plo = 0.0f, slo = 0.0f;
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();
     load_tile(Ks, Kg, kt);
@@ -197,33 +202,20 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
         const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
         l += w;
         wdp = fmaf(w, dp, wdp);
-      }
-    }
-  }
-  const float Dr = row < N ? wdp / l : 0.0f;
-
-  // extrema attached: the gradients of m and lo
-  float dm = 0.0f, dlo = 0.0f;
-  if (g_attached(a.mode) && (WK == WK_TRUNC || wk_kint(WK) || ((WK == WK_POT || WK == WK_POT_FLUSH) && g_ste(a.mode)))) {
-    for (int kt = 0; kt < kt_end; ++kt) {
-      __syncthreads();
-      load_tile(Ks, Kg, kt);
-      load_tile(Vs, Vg, kt);
-      __syncthreads();
-      for (int j = 0; j < TB; ++j) {
-        const float s = qdot<D>(Ks + j * D, q, u);
-        const float dp = qdot<D>(Vs + j * D, g, u);
-        if (kt * TB + j <= lim) {
-          const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
+        if (calib) {
           float gs, cm, clo;
           partials<WK>(s, w, rc, Tb, f.levels, dsc, minmax, g_ste(a.mode), gs, cm, clo);
-          const float dw = (dp - Dr) / l;
-          dm = fmaf(dw, cm, dm);
-          dlo = fmaf(dw, clo, dlo);
+          pm = fmaf(dp, cm, pm);
+          sm += cm;
+          plo = fmaf(dp, clo, plo);
+          slo += clo;
         }
       }
     }
   }
+  const float Dr = row < N ? wdp / l : 0.0f;
+  const float dm = calib && row < N ? fmaf(-Dr, sm, pm) / l : 0.0f;
+  const float dlo = calib && row < N ? fmaf(-Dr, slo, plo) / l : 0.0f;
   if (row < N && u == 0) {
     float* pk = a.dq + ((size_t)(b * f.H + h) * N + row) * D;
     pk[0] = M;

@@ -18,12 +18,17 @@ enum WeightKind : int {
   WK_KI_FLUSH = 7,     // K-interval, interpolation, below window -> 0
   WK_TRUNC = 8,        // exp(s - m) on the support s >= m - W, else 0
   WK_UNIF = 9,         // 1 on the support s >= m - W, else 0
-  WK_COUNT = 10
+  WK_POTR = 10,        // single-pass PoT, running integer anchor, saturate at L-1
+  WK_POTR_FLUSH = 11,  // single-pass PoT, e >= L -> 0
+  WK_COUNT = 12
 };
 
 // K-interval kinds (per-row grid table) and support kinds (truncation, uniform weighting).
 __host__ __device__ constexpr bool wk_kint(int wk) { return wk >= WK_KH && wk <= WK_KI_FLUSH; }
 __host__ __device__ constexpr bool wk_support(int wk) { return wk == WK_TRUNC || wk == WK_UNIF; }
+// Power-of-two weights, anchored at the row maximum (pre-pass) or at the running anchor.
+__host__ __device__ constexpr bool wk_running(int wk) { return wk == WK_POTR || wk == WK_POTR_FLUSH; }
+__host__ __device__ constexpr bool wk_pot(int wk) { return wk == WK_POT || wk == WK_POT_FLUSH || wk_running(wk); }
 
 // Everything a launch needs; passed by value as the kernel argument.
 struct FwdArgs {

@@ -57,12 +57,13 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   constexpr int KT = BN * KR, VT = BN * VR;  // bytes of one K / V tile buffer
   constexpr int KIW = (SK + NW - 1) / NW;    // direct-load instructions per wave per K tile (max)
   constexpr int VIW = (SV + NW - 1) / NW;
-  constexpr bool ANCH = (WK != WK_EXACT);
+  constexpr bool RUN = wk_running(WK);             // single-pass PoT: running integer anchor
+  constexpr bool ANCH = (WK != WK_EXACT) && !RUN;  // true-row-extrema pre-pass
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
-  constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
+  constexpr bool POT = wk_pot(WK);
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
   constexpr bool SUPPORT = wk_support(WK), UNIF = (WK == WK_UNIF);
-  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
+  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_POTR_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* const Tb = smem + 2 * KT + 2 * VT;  // K-interval tables
@@ -233,7 +234,16 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   f32x16 init16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
-  const int32_t pot_lo = 0x4B800000 - (a.levels - 1);  // bits of 2^24 - (L-1): the clip e <= L-1
+  // PoT rounds t = G - y to an integer in one FMA, G = 2^24 (pre-pass kinds: scores start at
+  // -M, so t = 2^24 + acc' c) or G = 1.5 * 2^23 (single pass: t = (G - A) + acc c, and G - A
+  // must be exact in fp32 for a negative integer anchor A too, which 2^24 - A is not).  In
+  // both cases t lies in [2^23, 2^24), bits(t) = bits(G) - e, and the low 16 bits are -e.
+  constexpr int32_t pot_bits = RUN ? 0x4B400000 : 0x4B800000;  // bits of G
+  constexpr float pot_g = RUN ? 12582912.0f : 16777216.0f;      // G
+  const int32_t pot_lo = pot_bits - (a.levels - 1);             // bits of G - (L-1): the clip e <= L-1
+  // Single-pass PoT: A = ceil(running max of s log2 e), an integer, and tb = G - A
+  float A = -__builtin_inff();
+  float tb = pot_g;
   const int L = a.levels;
   const float Kf = (float)a.levels;
 
@@ -264,22 +274,22 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
             }
           } else if (POT && !FLUSH) {
             // t = 2^24 + (acc - M) c = 2^24 - y, rounded to an integer by the FMA itself
-            const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
+            const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
             pk = pot_pair(t0, t1, pot_lo);
             if (DUMP) {
               i0 = 127u - ((pk >> 7) & 0x1FFu);
               i1 = 127u - ((pk >> 23) & 0x1FFu);
             }
           } else if (POT) {  // flush: e >= L -> 0
-            const float t0 = fmaf(x0, rc.c, 16777216.0f), t1 = fmaf(x1, rc.c, 16777216.0f);
-            const int32_t lo = 0x4B800000 - (L - 1);
+            const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
+            const int32_t lo = pot_bits - (L - 1);
             const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
             const uint32_t w0 = b0 < lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
             const uint32_t w1 = b1 < lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
             pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
             if (DUMP) {
-              i0 = b0 < lo ? 254u : (uint32_t)(0x4B800000 - b0);
-              i1 = b1 < lo ? 254u : (uint32_t)(0x4B800000 - b1);
+              i0 = b0 < lo ? 254u : (uint32_t)(pot_bits - b0);
+              i1 = b1 < lo ? 254u : (uint32_t)(pot_bits - b1);
             }
           } else if (KHARD) {
             // y = (M - acc) c; t = y + 2^23 rounds y: bits(t) = 0x4B000000 + l
@@ -356,6 +366,26 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     }
   };
 
+  // single-pass PoT: fold this tile's maximum into the anchor before its weights are formed;
+  // a rise of A by dA scales O and l, formed against the old anchor, by 2^-dA (exact)
+  auto run_anchor = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l, int kt, bool masked) {
+    float tm = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tm = fmaxf(tm, (!masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : -__builtin_inff());
+    const float An = fmaxf(A, __builtin_ceilf(half_max(tm) * rc.c));
+    if (__builtin_amdgcn_ballot_w64(An > A)) {
+      const float alpha = An > A ? (A > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(A - An)) : 0.0f) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      A = An;
+      tb = pot_g - An;
+    }
+  };
+
   // ---- main loop --------------------------------------------------------------
   f32x16 o[DB];
 #pragma unroll
@@ -377,6 +407,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
       // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
       const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
       if (WK == WK_EXACT) online_max(s, o, l);
+      if (RUN) run_anchor(s, o, l, t, false);
       u32x4 P[2];
       weights(s[0], 0, P, l, t, false);
       pv1(t & 1, 0, P, o);
@@ -391,6 +422,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
         if (last_masked) mask_fill(sm, t, -__builtin_inff());
         online_max(sm, o, l);
       }
+      if (RUN) run_anchor(s, o, l, t, last_masked);
       u32x4 P[2];
       weights(s[0], 0, P, l, t, last_masked);
       pv1(t & 1, 0, P, o);
@@ -422,7 +454,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     }
   if (hh == 0) {
     const size_t ri = (size_t)bh * N + row;
-    if (a.row_max) a.row_max[ri] = M * a.sc;
+    if (a.row_max) a.row_max[ri] = RUN ? A * 0.69314718055994531f : M * a.sc;  // single pass: A ln 2
     if (a.row_sum) a.row_sum[ri] = lt;
     if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
   }
@@ -454,6 +486,8 @@ hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
     case WK_EXACT_ANCH: return launch_one<D, WK_EXACT_ANCH>(a, st);
     case WK_POT: return launch_one<D, WK_POT>(a, st);
     case WK_POT_FLUSH: return launch_one<D, WK_POT_FLUSH>(a, st);
+    case WK_POTR: return launch_one<D, WK_POTR>(a, st);
+    case WK_POTR_FLUSH: return launch_one<D, WK_POTR_FLUSH>(a, st);
     case WK_KH: return launch_one<D, WK_KH>(a, st);
     case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
     case WK_KI: return launch_one<D, WK_KI>(a, st);

@@ -3,7 +3,9 @@
 // A correctness path for small fp32 problems, not a performance path: one
 // wave per workgroup, one lane per query row, scores as fp32 FMAs over d and
 // the weights kept in fp32.  The row extrema pre-pass and the weight
-// functions are the same as the MFMA kernels'.
+// functions are the same as the MFMA kernels'.  The single-pass PoT kind takes
+// 64-key tiles (its anchor moves once per 64 keys, as in the MFMA kernels): a
+// pass over a tile's scores for its maximum, then one for the weights.
 #include "qsa_common.h"
 #include "qsa_weights.h"
 
@@ -13,13 +15,18 @@ namespace {
 constexpr int BMF = 64;  // query rows per workgroup (one wave)
 constexpr int BNF = 32;  // keys per LDS tile
 
+template <int WK>
+constexpr int tile_keys() { return wk_running(WK) ? 64 : BNF; }
+
 template <int D, int WK>
 __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
-  constexpr bool ANCH = (WK != WK_EXACT);
+  constexpr bool RUN = wk_running(WK);
+  constexpr bool ANCH = (WK != WK_EXACT) && !RUN;
+  constexpr int BT = tile_keys<WK>();  // keys per LDS tile
   constexpr int SH = 8;  // log2(BMF * 4)
   extern __shared__ __align__(16) unsigned char smem[];
   float* Ks = (float*)smem;
-  float* Vs = Ks + BNF * D;
+  float* Vs = Ks + BT * D;
   unsigned char* Tb = (unsigned char*)(Vs + BNF * D);
 
   const int lane = threadIdx.x;
@@ -39,12 +46,12 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
   for (int c = 0; c < D; ++c) q[c] = row < N ? Qg[(size_t)row * D + c] : 0.0f;
 
   const int qend = min(q0 + BMF, N);
-  const int kt_end = a.causal ? ((qend - 1) / BNF + 1) : (N + BNF - 1) / BNF;
+  const int kt_end = a.causal ? ((qend - 1) / BT + 1) : (N + BT - 1) / BT;
   const int lim = a.causal ? min(row, N - 1) : N - 1;  // last key this row sees
 
   auto load_tile = [&](float* dst, const float* src, int kt) {
-    for (int e = lane; e < BNF * D; e += 64) {
-      const int key = kt * BNF + e / D;
+    for (int e = lane; e < BT * D; e += 64) {
+      const int key = kt * BT + e / D;
       dst[e] = key < N ? src[(size_t)key * D + e % D] : 0.0f;
     }
   };
@@ -61,8 +68,8 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
       __syncthreads();
       load_tile(Ks, Kg, kt);
       __syncthreads();
-      for (int j = 0; j < BNF; ++j) {
-        const int key = kt * BNF + j;
+      for (int j = 0; j < BT; ++j) {
+        const int key = kt * BT + j;
         if (key <= lim) {
           const float s = score(j);
           M = fmaxf(M, s);
@@ -78,12 +85,43 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
   for (int c = 0; c < D; ++c) o[c] = 0.0f;
   float l = 0.0f;
   const bool dump_row = a.grid_idx != nullptr && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N;
+  float A = -__builtin_inff();  // single-pass PoT: the running integer anchor, kept in rc.mc
 
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();
     load_tile(Ks, Kg, kt);
     load_tile(Vs, Vg, kt);
     __syncthreads();
+    if constexpr (RUN) {
+      // A = ceil(running max of s log2 e); a rise by dA scales what was formed by 2^-dA
+      float tm = -__builtin_inff();
+      for (int j = 0; j < BT; ++j)
+        if (kt * BT + j <= lim) tm = fmaxf(tm, score(j));
+      const float An = fmaxf(A, __builtin_ceilf(tm * rc.c));
+      if (An > A) {
+        const float alpha = A > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(A - An)) : 0.0f;
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] *= alpha;
+        A = An;
+        rc.mc = An;
+      }
+      for (int j = 0; j < BT; ++j) {
+        const int key = kt * BT + j;
+        const bool vis = key <= lim;
+        const float sj = score(j);
+        if (dump_row && key < N)
+          a.grid_idx[((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N + key] =
+              (uint8_t)(vis ? Weight<WK>::idx(sj, rc, a.levels) : 255u);
+        if (vis) {
+          const float w = Weight<WK>::template w<SH>(sj, rc, Tb, a.levels);
+          l += w;
+#pragma unroll
+          for (int c = 0; c < D; ++c) o[c] = fmaf(w, Vs[j * D + c], o[c]);
+        }
+      }
+      continue;
+    }
     float s[BNF];
 #pragma unroll
     for (int j = 0; j < BNF; ++j) s[j] = (kt * BNF + j <= lim) ? score(j) : -__builtin_inff();
@@ -120,14 +158,14 @@ __global__ __launch_bounds__(64) void fwd_f32(FwdArgs a) {
   if (row >= N) return;
   if (dump_row) {  // keys past the last tile are invisible to every row here (causal)
     uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
-    for (int key = kt_end * BNF; key < N; ++key) dst[key] = 255u;
+    for (int key = kt_end * BT; key < N; ++key) dst[key] = 255u;
   }
   float* Og = (float*)a.o + (size_t)(b * a.H + h) * N * D;
   const float inv = a.vd / l;
 #pragma unroll
   for (int c = 0; c < D; ++c) Og[(size_t)row * D + c] = o[c] * inv;
   const size_t ri = (size_t)bh * N + row;
-  if (a.row_max) a.row_max[ri] = M * a.sc;
+  if (a.row_max) a.row_max[ri] = RUN ? A * 0.69314718055994531f : M * a.sc;  // single pass: A ln 2
   if (a.row_sum) a.row_sum[ri] = l;
   if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
 }
@@ -137,7 +175,7 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   FwdArgs a = a0;
   a.n_qtiles = (a.N + BMF - 1) / BMF;
   a.total_blocks = a.B * a.H * a.n_qtiles;
-  const size_t lds = 2 * (size_t)BNF * D * 4 + table_bytes(WK, BMF, a.levels);
+  const size_t lds = 2 * (size_t)tile_keys<WK>() * D * 4 + table_bytes(WK, BMF, a.levels);
   auto kern = fwd_f32<D, WK>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -154,6 +192,8 @@ hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
     case WK_EXACT_ANCH: return launch_one<D, WK_EXACT_ANCH>(a, st);
     case WK_POT: return launch_one<D, WK_POT>(a, st);
     case WK_POT_FLUSH: return launch_one<D, WK_POT_FLUSH>(a, st);
+    case WK_POTR: return launch_one<D, WK_POTR>(a, st);
+    case WK_POTR_FLUSH: return launch_one<D, WK_POTR_FLUSH>(a, st);
     case WK_KH: return launch_one<D, WK_KH>(a, st);
     case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
     case WK_KI: return launch_one<D, WK_KI>(a, st);

@@ -68,12 +68,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
-  constexpr bool ANCH = (WK != WK_EXACT);
+  constexpr bool RUN = wk_running(WK);                // single-pass PoT: running integer anchor
+  constexpr bool ANCH = (WK != WK_EXACT) && !RUN;     // read the pre-pass extrema
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
-  constexpr bool POT = (WK == WK_POT || WK == WK_POT_FLUSH);
+  constexpr bool POT = wk_pot(WK);
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
   constexpr bool SUPPORT = wk_support(WK), UNIF = (WK == WK_UNIF);
-  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
+  constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_POTR_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
   constexpr bool PV8 = POT;
   constexpr int SK = D / 16;                          // 16-byte slots per K row (swizzled)
   constexpr int SV = PV8 ? D / 16 : (D / 8 + 4);  // fp8 V rows (swizzled, unpadded), or bf16 rows (stride 64 mod 256)
@@ -315,9 +316,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // 2^(L-15-e) is the bf8 byte (L - e) << 2
   const int ec = FLUSH ? L : L - 1;
   const uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(-ec);  // -ec, twice (int16)
-  const int32_t pot_lo = 0x4B800000 - ec;                               // bits of 2^24 - ec
+  // the exponent comes from t = G - y rounded by one FMA (see weights8): G = 2^24 for the
+  // pre-pass kinds, 1.5 * 2^23 for the single pass (G - A must be exact for negative integer
+  // anchors, which 2^24 - A is not); bits(t) = bits(G) - e either way
+  constexpr int32_t pot_bits = RUN ? 0x4B400000 : 0x4B800000;
+  constexpr float pot_g = RUN ? 12582912.0f : 16777216.0f;
+  const int32_t pot_lo = pot_bits - ec;                                 // bits of G - ec
   const uint32_t pot_add = 0x00010001u * (uint32_t)(4 * L * 257);     // 4L in both bytes of a half
   const float Kf = (float)a.levels;
+  // Single-pass PoT: A = ceil(running max of s log2 e), an integer, and tb = G - A, so that
+  // the weight formation below computes G - (A - s log2 e) with the FMA that rounds it.  The
+  // kinds anchored by the pre-pass start their scores at -M instead and keep tb = G = 2^24.
+  float A = -__builtin_inff();
+  float tb = pot_g;
 
   // bf16 weights of 32-key block kb (exact / K-interval), as in the bf16 kernel
   auto weights16 = [&](const f32x16& sb, int kb, u32x4 (&P)[2], float& l, int kt, bool masked) {
@@ -400,8 +411,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   };
 
   // PoT weights of a whole 64-key tile as bf8 bytes (P8); their row sum goes to rs by an MMA.
-  // t = 2^24 - y rounded to an integer (y = (m - s) log2 e >= 0, the FMA rounds to nearest
-  // even): the low 16 bits of its pattern are -e.  For four elements r0..r0+3 the clamped
+  // t = G - y rounded to an integer (y = (m - s) log2 e >= 0, or A - s log2 e for the single
+  // pass; the FMA rounds to nearest even): the low 16 bits of its pattern are -e.  For four elements r0..r0+3 the clamped
   // pairs (-e0, -e1) and (-e2, -e3) become the bytes 4(L - e) in the order r0, r0+2, r0+1,
   // r0+3 by two v_pk_mad_u16: 4(-e) + 4L*257 gives byte 0 and a carry-free 4L in byte 1 of
   // each half, then 1024(-e') adds the second pair's bytes in byte 1.
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #pragma unroll
       for (int hp = 0; hp < 2; ++hp) {
         const int r = r0 + 2 * hp;
-        uint32_t t0 = fbits(fmaf(s[kb][r], rc.c, 16777216.0f)), t1 = fbits(fmaf(s[kb][r + 1], rc.c, 16777216.0f));
+        uint32_t t0 = fbits(fmaf(s[kb][r], rc.c, tb)), t1 = fbits(fmaf(s[kb][r + 1], rc.c, tb));
         if (WIDE || DUMP) {  // clamp in 32 bits: exact for any y
           t0 = (uint32_t)max((int32_t)t0, pot_lo);
           t1 = (uint32_t)max((int32_t)t1, pot_lo);
@@ -458,6 +469,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
   };
 
+  // Single-pass PoT: fold the maximum of the next tile into the anchor before its weights are
+  // formed; when A rises by dA, O and the row sums, whose weights were formed against the old
+  // anchor, are scaled by 2^-dA (exact).  The row-sum MMA leaves the sum of query q(l) in lane
+  // l (q = l, l-16, l-16, l-32 for the four 16-lane groups; see the epilogue), whose factor
+  // is fetched from lane q(l).
+  auto run_anchor = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], int kt, bool masked) __attribute__((always_inline)) {
+    float tm = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tm = fmaxf(tm, (!masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : -__builtin_inff());
+    const float An = fmaxf(A, __builtin_ceilf(half_max(tm) * rc.c));
+    if (__builtin_amdgcn_ballot_w64(An > A)) {
+      const float alpha = An > A ? (A > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(A - An)) : 0.0f) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      const int ql = lane < 16 ? lane : (lane < 48 ? lane - 16 : lane - 32);
+      rs *= bitsf(__builtin_amdgcn_ds_bpermute(4 * ql, (int)fbits(alpha)));
+      A = An;
+      tb = pot_g - An;
+    }
+  };
+
   // ---- main loop --------------------------------------------------------------
   f32x16 o[DB];
 #pragma unroll
@@ -496,7 +531,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       // the loads iteration -1 would have issued
       load_k(min(3, T - 1), 0);
       load_v(min(2, T - 1), 2);
-      if (wlast >= 0) weights8(s0, P8c, 0, wlast == 0 && last_masked);
+      if (wlast >= 0) {
+        if (RUN) run_anchor(s0, o, 0, wlast == 0 && last_masked);
+        weights8(s0, P8c, 0, wlast == 0 && last_masked);
+      }
     }
     int t = 0;
     // Every iteration issues the same loads, so that neither the prefetch nor the wait needs a
@@ -517,6 +555,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       read_v8(b1, va);
       prefetch_to(b0, b1);
       const f32x16 sn0 = qk1(b2, 0, init16);
+      if (RUN) run_anchor(s, o, t + 1, false);
       weights8(s, P8c, t + 1, false);
       const f32x16 sn1 = qk1(b2, 1, init16);
       s[0] = sn0;
@@ -538,6 +577,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
         mma_pv8(va, P8c, o);
         read_v8(b1, va);
         prefetch_to(b0, b1);
+        if (RUN) run_anchor(s, o, t + 1, last_masked);
         weights8(s, P8c, t + 1, last_masked);
       } else if (t == wlast) {
         mma_pv8(va, P8c, o);
@@ -614,7 +654,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
   if (hh == 0) {
     const size_t ri = (size_t)bh * N + row;
-    if (a.row_max) a.row_max[ri] = M * a.sc;
+    if (a.row_max) a.row_max[ri] = RUN ? A * 0.69314718055994531f : M * a.sc;  // single pass: A ln 2
     if (a.row_sum) a.row_sum[ri] = PV8 ? __builtin_ldexpf(lt, 15 - L) : lt;  // PoT P carries 2^(L-15)
     if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
   }
@@ -836,13 +876,14 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   FwdArgs a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.total_blocks = a.B * a.H * a.n_qtiles;
-  constexpr bool PV8 = (WK == WK_POT || WK == WK_POT_FLUSH);
-  constexpr bool ANCH = WK != WK_EXACT;
+  constexpr bool PV8 = wk_pot(WK);
+  constexpr bool ANCH = WK != WK_EXACT && !wk_running(WK);
   constexpr int SK = D / 16, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
   const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
   // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
-  // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does
+  // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does (the single-pass
+  // anchor adds less than 1 to y, inside the margin to 2^15)
   const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
   const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false>
                                 : wide ? (const void*)fwd_fp8<D, WK, false, PV8> : (const void*)fwd_fp8<D, WK, false, false>;
@@ -878,6 +919,8 @@ hipError_t launch_d(const FwdArgs& a, int wk, hipStream_t st) {
     case WK_EXACT_ANCH: return launch_one<D, WK_EXACT_ANCH>(a, st);
     case WK_POT: return launch_one<D, WK_POT>(a, st);
     case WK_POT_FLUSH: return launch_one<D, WK_POT_FLUSH>(a, st);
+    case WK_POTR: return launch_one<D, WK_POTR>(a, st);
+    case WK_POTR_FLUSH: return launch_one<D, WK_POTR_FLUSH>(a, st);
     case WK_KH: return launch_one<D, WK_KH>(a, st);
     case WK_KH_FLUSH: return launch_one<D, WK_KH_FLUSH>(a, st);
     case WK_KI: return launch_one<D, WK_KI>(a, st);

@@ -91,6 +91,10 @@ template <bool FLUSH> struct PotW {
 };
 template <> struct Weight<WK_POT> : PotW<false> {};
 template <> struct Weight<WK_POT_FLUSH> : PotW<true> {};
+// Single-pass PoT: the same exponent against the running integer anchor A, which the kernel
+// keeps in RowC::mc (with c = scale log2 e, y = A - acc c).
+template <> struct Weight<WK_POTR> : PotW<false> {};
+template <> struct Weight<WK_POTR_FLUSH> : PotW<true> {};
 
 // K-interval, hard rounding.  t = y + 2^23 rounds y to the nearest integer
 // (ties to even) inside the float: bits(t) = 0x4B000000 + l.  The clip l <= K

@@ -29,6 +29,9 @@ KI4W = dict(kind="kint", levels=4, window=8.0, interp=True)
 KI16W = dict(kind="kint", levels=16, window=8.0, interp=True)
 KH4WF = dict(kind="kint", levels=4, window=3.0, flush=True)
 KI4WF = dict(kind="kint", levels=4, window=3.0, interp=True, flush=True)
+POTR8 = dict(kind="pot_running", levels=8)
+POTR16 = dict(kind="pot_running", levels=16)
+POTR4F = dict(kind="pot_running", levels=4, flush=True)
 TRUNC2 = dict(kind="trunc", window=2.0)
 UNIF2 = dict(kind="uniform", window=2.0)
 
@@ -76,7 +79,7 @@ def gpu_call(x, dev_t, var, *, causal, idx_window=None, stats=False):
         grid = torch.full((B, H, nr, N), 77, dtype=torch.uint8, device=q.device)
     st = {}
     if stats:
-        for key in ("row_max", "row_sum") + (("row_lo",) if var["kind"] != "exact" else ()):
+        for key in ("row_max", "row_sum") + (("row_lo",) if var["kind"] not in ("exact", "pot_running") else ()):
             st[key] = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
     o = qsa.attn_fwd_ex(q, k, v, causal=causal, q_descale=x.q_descale if q.dtype == torch.float8_e4m3fn else 0.0,
                         k_descale=x.k_descale if q.dtype == torch.float8_e4m3fn else 0.0,
@@ -86,8 +89,10 @@ def gpu_call(x, dev_t, var, *, causal, idx_window=None, stats=False):
     return o, grid, st
 
 
-def run_parity(wl, var, *, windows=None, heads=None, tol=None, x=None, dev_t=None, f64=None, verbose=True):
-    """Launch the full problem once per row window; compare the chosen (b, h)."""
+def run_parity(wl, var, *, windows=None, heads=None, tol=None, x=None, dev_t=None, f64=None, verbose=True,
+               anchor_frac=0.03):
+    """Launch the full problem once per row window; compare the chosen (b, h).  anchor_frac:
+    the largest share of rows whose single-pass anchor may round either way."""
     x = x if x is not None else qin.make_inputs(wl)
     dev_t = dev_t if dev_t is not None else to_gpu(x)
     qf, kf, vf = f64 if f64 is not None else decoded(x)
@@ -113,7 +118,9 @@ def run_parity(wl, var, *, windows=None, heads=None, tol=None, x=None, dev_t=Non
             rep.merge(r)
     if verbose:
         print(f"[parity] {name(var)}: rows={rep.rows} agree={rep.idx_agree:.6f} disagree={rep.idx_disagree} "
-              f"amb_rows={rep.amb_rows} max_rel_err={rep.max_rel_err:.3e}", flush=True, file=sys.stderr)
+              f"amb_rows={rep.amb_rows} anchor_amb_rows={rep.anchor_amb_rows} max_rel_err={rep.max_rel_err:.3e}",
+              flush=True, file=sys.stderr)
+    parity.check_anchor_rows(rep, anchor_frac)
     return rep
 
 

@@ -49,7 +49,7 @@ def test_header_constants_match_binding():
     src = open(HEADER).read()
     for name, val in [("QSA_EXACT", qsa.EXACT), ("QSA_KINT", qsa.KINT), ("QSA_POT", qsa.POT),
                       ("QSA_EXACT_ANCHORED", qsa.EXACT_ANCHORED), ("QSA_TRUNC", qsa.TRUNC),
-                      ("QSA_UNIFORM", qsa.UNIFORM), ("QSA_DT_F32", qsa.DT_F32),
+                      ("QSA_UNIFORM", qsa.UNIFORM), ("QSA_POT_RUNNING", qsa.POT_RUNNING), ("QSA_DT_F32", qsa.DT_F32),
                       ("QSA_DT_BF16", qsa.DT_BF16), ("QSA_DT_FP8_E4M3", qsa.DT_FP8_E4M3),
                       ("QSA_GRAD_STE_POST", qsa.GRADS["ste_post"]), ("QSA_GRAD_EXACT", qsa.GRADS["exact"]),
                       ("QSA_GRAD_EXACT_DETACHED", qsa.GRADS["exact_detached"]),
@@ -69,7 +69,7 @@ def test_valid_arguments():
                        (qsa.KINT | qsa.F_INTERP, 16, 0.0), (qsa.KINT | qsa.F_WINDOW, 16, 8.0),
                        (qsa.KINT | qsa.F_WINDOW | qsa.F_FLUSH | qsa.F_INTERP, 64, 8.0),
                        (qsa.POT | qsa.F_FLUSH, 64, 0.0), (qsa.POT, 1, 0.0), (qsa.TRUNC, 0, 2.0),
-                       (qsa.UNIFORM, 0, 0.5)]:
+                       (qsa.UNIFORM, 0, 0.5), (qsa.POT_RUNNING, 2, 0.0), (qsa.POT_RUNNING | qsa.F_FLUSH, 64, 0.0)]:
         assert v(variant=var, k_levels=kl, window=w) == qsa.OK, (var, kl, w)
     assert v(d=128, N=1, H=64, Hkv=8) == qsa.OK
     assert v(dtype=qsa.DT_F32) == qsa.OK
@@ -81,7 +81,11 @@ def test_valid_arguments():
     (dict(d=96), qsa.ERR_UNSUPPORTED), (dict(d=256), qsa.ERR_UNSUPPORTED),
     (dict(B=1024, H=64, N=65536, d=128), qsa.ERR_SHAPE),
     (dict(dtype=3), qsa.ERR_PARAM), (dict(dtype=-1), qsa.ERR_PARAM),
-    (dict(variant=6), qsa.ERR_PARAM), (dict(variant=qsa.POT | (1 << 8)), qsa.ERR_PARAM),
+    (dict(variant=7), qsa.ERR_PARAM), (dict(variant=qsa.POT | (1 << 8)), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT_RUNNING, k_levels=1), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT_RUNNING, k_levels=65), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT_RUNNING, k_levels=17, dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT_RUNNING | qsa.F_INTERP, k_levels=8), qsa.ERR_PARAM),
     (dict(variant=qsa.TRUNC, window=0.0), qsa.ERR_PARAM), (dict(variant=qsa.UNIFORM, window=-2.0), qsa.ERR_PARAM),
     (dict(variant=qsa.TRUNC, window=math.inf), qsa.ERR_PARAM), (dict(variant=qsa.UNIFORM, window=math.nan), qsa.ERR_PARAM),
     (dict(variant=qsa.TRUNC | qsa.F_FLUSH, window=2.0), qsa.ERR_PARAM),
@@ -132,6 +136,7 @@ def _fwd_ex(opts, **kw):
     (dict(v_descale=-1.0), dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
     (dict(k_descale=math.inf), dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_PARAM),
     (dict(row_lo=8), dict(variant=qsa.EXACT), qsa.ERR_PARAM),
+    (dict(row_lo=8), dict(variant=qsa.POT_RUNNING), qsa.ERR_PARAM),
     (dict(grid_idx=8, idx_row0=0, idx_rows=0), {}, qsa.ERR_SHAPE),
     (dict(grid_idx=8, idx_row0=-1, idx_rows=4), {}, qsa.ERR_SHAPE),
     (dict(grid_idx=8, idx_row0=98, idx_rows=4), {}, qsa.ERR_SHAPE),
@@ -168,6 +173,7 @@ def _bwd(ptrs=(1, 1, 1, 1, 1, 1, 1), grad=0, scale=0.0, **kw):
     (dict(dtype=qsa.DT_FP8_E4M3), qsa.ERR_UNSUPPORTED), (dict(grad=-1), qsa.ERR_PARAM),
     (dict(grad=5), qsa.ERR_PARAM), (dict(scale=-1.0), qsa.ERR_PARAM), (dict(scale=math.nan), qsa.ERR_PARAM),
     (dict(variant=qsa.KINT, k_levels=0), qsa.ERR_PARAM), (dict(variant=qsa.TRUNC, window=0.0), qsa.ERR_PARAM),
+    (dict(variant=qsa.POT_RUNNING), qsa.ERR_UNSUPPORTED),
 ])
 def test_backward_validation_before_any_hip_call(kw, status):
     assert _bwd(**kw) == status

@@ -8,7 +8,9 @@ edge, or a row whose maximum or minimum is tied within EDGE_S, may take the othe
 float32.  Rows holding one get dO = 0 on both sides: such a row adds exactly zero to every
 gradient (its dV terms are P * 0; dP and D vanish, so its dS does in every mode), so the
 comparison is exact-decision everywhere else.  Tolerance: max |gpu - oracle| <= TOL times
-max |oracle| per tensor (float32 sums of at most N terms).
+max(max |oracle|, FLOOR) per tensor (float32 sums of at most N terms; the floor covers
+gradients that vanish exactly, as with a single visible key, where float32 leaves rounding
+residue of order 1e-8 on inputs of order 1).
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ pytestmark = pytest.mark.gpu
 EDGE_Y = 2e-4     # grid-coordinate units
 EDGE_S = 2e-5     # score units
 TOL = 2e-4
+FLOOR = 1e-3
 MODES = ["ste_post", "ste_pre", "ste_pre_detached", "exact", "exact_detached"]
 KINDS = [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KI4W, gc.KH4WF,
          gc.KI4WF, gc.TRUNC2, gc.UNIF2]
@@ -112,7 +115,7 @@ def _case(wl, var, grad, heads=None):
         hs = sorted({h for bb, h in heads if bb == b})
         kvs = sorted({h // group for h in hs})
         for name, got, ref in (("dQ", dq[b][hs], oq[hs]), ("dK", dk[b][kvs], ok_[kvs]), ("dV", dv[b][kvs], ov[kvs])):
-            scale = max(np.abs(ref).max(), 1e-30)
+            scale = max(np.abs(ref).max(), FLOOR)
             err = np.abs(got - ref).max() / scale
             worst[name] = max(worst.get(name, 0.0), err)
     print(f"[bwd]   rel err " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in worst.items()), flush=True, file=sys.stderr)

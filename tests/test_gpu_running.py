@@ -1,0 +1,138 @@
+"""GPU parity of the single-pass power-of-two weights (kind ``pot_running``, no row-maximum
+pre-pass) against the oracle's closed form, through the C ABI, on every kernel (fp32, bf16,
+fp8): the tiny fp32 workload, the GPT-2-shaped and 2K sink workloads, the 8K fp8 workload
+(seeded row windows, full size), ragged tails, wide level counts and score ranges, the row
+statistics (final anchor and row sum) and determinism."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_softmax_approximation_amd as qsa
+from quantized_softmax_approximation_amd import inputs as qin
+from tests import gpu_cases as gc
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+RUN_VARS = [gc.POTR8, gc.POTR16, gc.POTR4F]
+
+
+@pytest.mark.parametrize("var", RUN_VARS, ids=gc.name)
+def test_tiny_fp32(var):
+    gc.run_parity(qin.WORKLOADS["tiny"], var)
+
+
+@pytest.fixture(scope="module")
+def gpt2():
+    wl = qin.WORKLOADS["gpt2"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("var", RUN_VARS, ids=gc.name)
+def test_gpt2(gpt2, var):
+    wl, x, dev_t, f64 = gpt2
+    gc.run_parity(wl, var, heads=[(b, h) for b in (0, 7) for h in range(12)], x=x, dev_t=dev_t, f64=f64)
+
+
+@pytest.mark.parametrize("var", [gc.POTR8, gc.POTR16], ids=gc.name)
+def test_pot2k_sink(var):
+    wl = qin.WORKLOADS["pot2k"]
+    x = qin.make_inputs(wl)
+    gc.run_parity(wl, var, heads=[(0, 0), (2, 17), (3, 31)], x=x)
+
+
+@pytest.fixture(scope="module")
+def fp8_8k():
+    wl = qin.WORKLOADS["fp8_8k"]
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("var", RUN_VARS, ids=gc.name)
+def test_fp8_8k_sampled(fp8_8k, var, causal):
+    wl, x, dev_t, f64 = fp8_8k
+    wl = wl.replace(causal=causal)
+    gc.run_parity(wl, var, heads=[(0, 0), (0, 13), (0, 31)], windows=gc.sample_windows(wl.N, n=4, seed=7),
+                  x=x, dev_t=dev_t, f64=f64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 333])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged(dtype, N, causal):
+    for d in (64, 128):
+        wl = qin.custom(f"run{dtype}{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype=dtype, causal=causal, sigma_qk=1.5,
+                        seed=3 * N + d)
+        x = qin.make_inputs(wl)
+        dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
+        for var in (gc.POTR8, gc.POTR4F):
+            gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 100, 200])
+def test_ragged_fp32(N):
+    wl = qin.custom(f"runf32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
+    x = qin.make_inputs(wl)
+    for var in (gc.POTR8, gc.POTR4F):
+        gc.run_parity(wl, var, x=x, verbose=False)
+
+
+def test_level_counts_and_wide_scores():
+    wl = qin.custom("runlevels", B=1, H=2, N=300, d=64, dtype="bf16", causal=False, sigma_qk=2.0, seed=3)
+    x = qin.make_inputs(wl)
+    for var in (dict(kind="pot_running", levels=64), dict(kind="pot_running", levels=2),
+                dict(kind="pot_running", levels=2, flush=True)):
+        gc.run_parity(wl, var, x=x)
+    # logit std 36: score gaps of hundreds of log2 units, every level clipped or flushed.  The
+    # fp32 score error there reaches 1e-2 log2 units, so more anchors may round either way
+    # (with gaps in the thousands it exceeds one unit and no anchor is decided at all)
+    for dtype in ("bf16", "fp8"):
+        wl = qin.custom(f"runwide_{dtype}", B=1, H=2, N=200, d=128, dtype=dtype, causal=True, sigma_qk=6.0,
+                        seed=11)
+        x = qin.make_inputs(wl)
+        for var in (gc.POTR8, gc.POTR16, gc.POTR4F):
+            rep = gc.run_parity(wl, var, x=x, anchor_frac=0.25)
+            assert rep.rows - rep.anchor_amb_rows >= 300
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_row_stats_are_the_final_anchor_and_sum(dtype):
+    d = 128 if dtype != "f32" else 64
+    wl = qin.custom(f"runstats_{dtype}", B=1, H=2, N=257, d=d, dtype=dtype, causal=True, sigma_qk=1.5, seed=8)
+    x = qin.make_inputs(wl)
+    dev_t = gc.to_gpu(x)
+    qf, kf, vf = gc.decoded(x)
+    for var in (gc.POTR8, gc.POTR4F):
+        o, _, st = gc.gpu_call(x, dev_t, var, causal=True, stats=True)
+        for h in range(2):
+            ref = oracle.head_rows(qf[0, h], kf[0, h], vf[0, h], causal=True, detail=True, **var)
+            A = st["row_max"][0, h].cpu().numpy() / math.log(2.0)
+            # the anchor is an integer; it may sit one off where the row maximum is within the
+            # fp32 band of an integer (those rows are the protocol's anchor-ambiguous ones)
+            np.testing.assert_allclose(A, np.rint(A), atol=1e-4)
+            assert np.mean(np.rint(A) == ref["A"]) >= 0.99
+            rep, _ = parity.compare_head(var, qf[0, h], kf[0, h], vf[0, h], np.arange(257),
+                                         o[0, h].float().cpu().numpy(), causal=True,
+                                         tol=3e-2 if dtype == "fp8" else 1e-2,
+                                         l_gpu=st["row_sum"][0, h].cpu().numpy())
+            parity.check_anchor_rows(rep)
+
+
+def test_deterministic_and_no_row_lo():
+    wl = qin.custom("rundet", B=2, H=8, Hkv=2, N=300, d=128, dtype="bf16", causal=True, sigma_qk=1.5, seed=9)
+    x = qin.make_inputs(wl)
+    q, k, v = gc.to_gpu(x)
+    a = qsa.attn_fwd(q, k, v, causal=True, **gc.POTR8)
+    b = qsa.attn_fwd(q, k, v, causal=True, **gc.POTR8)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    lo = torch.empty(2, 8, 300, device="cuda")
+    with pytest.raises(qsa.QSAError):
+        qsa.attn_fwd_ex(q, k, v, causal=True, row_lo=lo, **gc.POTR8)
+    with pytest.raises(qsa.QSAError):
+        qsa.attn_bwd(q, k, v, q, causal=True, **gc.POTR8)

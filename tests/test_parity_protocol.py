@@ -31,6 +31,27 @@ def emulate(var, q, k, v, causal):
         c = F(sc * F(1.4426950408889634))
         w = np.exp2((acc * c - M[:, None] * c).astype(F))
         idx[vis] = 0
+    elif kind == "pot_running":
+        # anchor after each 64-key tile: ceil of the fp32 product (running raw max) * c; the
+        # exponent rounds A - acc c exactly once (one FMA), as the kernels do
+        L = var["levels"]
+        c = F(sc * F(1.4426950408889634))
+        raw = np.where(vis, acc, -np.inf).astype(F)
+        nt = (N + 63) // 64
+        cm = np.maximum.accumulate(np.stack([raw[:, j * 64:(j + 1) * 64].max(1) for j in range(nt)], 1), 1)
+        A = np.ceil((cm * c).astype(F)).astype(np.float64)
+        Aj = np.repeat(A, 64, axis=1)[:, :N]
+        e = np.rint(Aj - acc.astype(np.float64) * np.float64(c))
+        shift = A[:, -1:] - Aj
+        if var.get("flush"):
+            kept = e <= L - 1
+            w = np.where(kept, np.exp2(-np.minimum(e + shift, 126)), 0).astype(F)
+            idx = np.where(kept, e, 254).astype(np.uint8)
+        else:
+            e = np.clip(e, 0, L - 1)
+            w = np.exp2(-(e + shift)).astype(F)
+            idx = e.astype(np.uint8)
+        w = np.where(vis, w, 0).astype(F)
     elif kind == "pot":
         L = var["levels"]
         c = F(sc * F(1.4426950408889634))
@@ -78,6 +99,8 @@ def emulate(var, q, k, v, causal):
 
 
 VARS = [dict(kind="exact"), dict(kind="pot", levels=8), dict(kind="pot", levels=4, flush=True),
+        dict(kind="pot_running", levels=8), dict(kind="pot_running", levels=4, flush=True),
+        dict(kind="pot_running", levels=16),
         dict(kind="kint", levels=4), dict(kind="kint", levels=16, interp=True),
         dict(kind="kint", levels=4, window=8.0), dict(kind="kint", levels=16, window=8.0, flush=True),
         dict(kind="kint", levels=4, window=3.0, interp=True, flush=True)]
