@@ -240,9 +240,15 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   // both cases t lies in [2^23, 2^24), bits(t) = bits(G) - e, and the low 16 bits are -e.
   constexpr int32_t pot_bits = RUN ? 0x4B400000 : 0x4B800000;  // bits of G
   constexpr float pot_g = RUN ? 12582912.0f : 16777216.0f;      // G
-  const int32_t pot_lo = pot_bits - (a.levels - 1);             // bits of G - (L-1): the clip e <= L-1
-  // Single-pass PoT: A = ceil(running max of s log2 e), an integer, and tb = G - A
-  float A = -__builtin_inff();
+  int32_t pot_lo = pot_bits - (a.levels - 1);                   // bits of G - (L-1): the clip e <= L-1
+  // Single-pass PoT: A = ceil(running max of s log2 e), an integer.  The weights are formed
+  // against a lagging integer anchor Aw <= A (tb = G - Aw) with the clip moved by the lag
+  // dl = A - Aw (pot_lo = bits(G) - (L-1) + dl), so every weight carries the same factor 2^dl
+  // relative to A while Aw stays; O and l are rescaled only when Aw moves, on the first tile
+  // and when the lag would pass 32 (bf16 weights up to 2^32 and their sums stay well inside
+  // the exponent range).
+  float A = -__builtin_inff(), Aw = -__builtin_inff();
+  int dlag = 0;
   float tb = pot_g;
   const int L = a.levels;
   const float Kf = (float)a.levels;
@@ -277,19 +283,19 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
             const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
             pk = pot_pair(t0, t1, pot_lo);
             if (DUMP) {
-              i0 = 127u - ((pk >> 7) & 0x1FFu);
-              i1 = 127u - ((pk >> 23) & 0x1FFu);
+              i0 = 127u - ((pk >> 7) & 0x1FFu) + (uint32_t)dlag;  // against the running anchor
+              i1 = 127u - ((pk >> 23) & 0x1FFu) + (uint32_t)dlag;
             }
           } else if (POT) {  // flush: e >= L -> 0
             const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
-            const int32_t lo = pot_bits - (L - 1);
+            const int32_t lo = pot_lo;
             const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
             const uint32_t w0 = b0 < lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
             const uint32_t w1 = b1 < lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
             pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
             if (DUMP) {
-              i0 = b0 < lo ? 254u : (uint32_t)(pot_bits - b0);
-              i1 = b1 < lo ? 254u : (uint32_t)(pot_bits - b1);
+              i0 = b0 < lo ? 254u : (uint32_t)(pot_bits - b0 + dlag);
+              i1 = b1 < lo ? 254u : (uint32_t)(pot_bits - b1 + dlag);
             }
           } else if (KHARD) {
             // y = (M - acc) c; t = y + 2^23 rounds y: bits(t) = 0x4B000000 + l
@@ -367,7 +373,8 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   };
 
   // single-pass PoT: fold this tile's maximum into the anchor before its weights are formed;
-  // a rise of A by dA scales O and l, formed against the old anchor, by 2^-dA (exact)
+  // when the weight anchor Aw has to move, O and l, formed against the old Aw, are scaled by
+  // 2^(Aw_old - Aw) (exact)
   auto run_anchor = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l, int kt, bool masked) {
     float tm = -__builtin_inff();
 #pragma unroll
@@ -376,14 +383,18 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
       for (int r = 0; r < 16; ++r)
         tm = fmaxf(tm, (!masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : -__builtin_inff());
     const float An = fmaxf(A, __builtin_ceilf(half_max(tm) * rc.c));
-    if (__builtin_amdgcn_ballot_w64(An > A)) {
-      const float alpha = An > A ? (A > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(A - An)) : 0.0f) : 1.0f;
+    if (__builtin_amdgcn_ballot_w64(An - Aw > 32.0f)) {  // Aw = -inf before the first tile
+      const bool move = An - Aw > 32.0f;
+      const float alpha = move ? (Aw > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(Aw - An)) : 0.0f) : 1.0f;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      A = An;
-      tb = pot_g - An;
+      Aw = move ? An : Aw;
+      tb = pot_g - Aw;
     }
+    A = An;
+    dlag = (int)(A - Aw);
+    pot_lo = pot_bits - (a.levels - 1) + dlag;
   };
 
   // ---- main loop --------------------------------------------------------------
@@ -455,7 +466,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   if (hh == 0) {
     const size_t ri = (size_t)bh * N + row;
     if (a.row_max) a.row_max[ri] = RUN ? A * 0.69314718055994531f : M * a.sc;  // single pass: A ln 2
-    if (a.row_sum) a.row_sum[ri] = lt;
+    if (a.row_sum) a.row_sum[ri] = RUN ? __builtin_ldexpf(lt, -dlag) : lt;  // single pass: against A
     if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
   }
 #endif

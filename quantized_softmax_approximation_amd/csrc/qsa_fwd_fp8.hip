@@ -315,19 +315,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   // PoT: e is clamped to ec = L-1 (or L with flush, whose level weighs 0); the weight
   // 2^(L-15-e) is the bf8 byte (L - e) << 2
   const int ec = FLUSH ? L : L - 1;
-  const uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(-ec);  // -ec, twice (int16)
+  uint32_t pot_clip = 0x00010001u * (uint32_t)(uint16_t)(-ec);  // -ec, twice (int16)
   // the exponent comes from t = G - y rounded by one FMA (see weights8): G = 2^24 for the
   // pre-pass kinds, 1.5 * 2^23 for the single pass (G - A must be exact for negative integer
   // anchors, which 2^24 - A is not); bits(t) = bits(G) - e either way
   constexpr int32_t pot_bits = RUN ? 0x4B400000 : 0x4B800000;
   constexpr float pot_g = RUN ? 12582912.0f : 16777216.0f;
-  const int32_t pot_lo = pot_bits - ec;                                 // bits of G - ec
+  int32_t pot_lo = pot_bits - ec;                                       // bits of G - ec
   const uint32_t pot_add = 0x00010001u * (uint32_t)(4 * L * 257);     // 4L in both bytes of a half
   const float Kf = (float)a.levels;
-  // Single-pass PoT: A = ceil(running max of s log2 e), an integer, and tb = G - A, so that
-  // the weight formation below computes G - (A - s log2 e) with the FMA that rounds it.  The
-  // kinds anchored by the pre-pass start their scores at -M instead and keep tb = G = 2^24.
-  float A = -__builtin_inff();
+  // Single-pass PoT: A = ceil(running max of s log2 e), an integer.  The weights are formed
+  // against a lagging integer anchor Aw <= A (tb = G - Aw, so the FMA below rounds
+  // G - (Aw - s log2 e) = G - e_w), with the clip moved by the lag dl = A - Aw: e_w <= ec - dl,
+  // i.e. e = e_w + dl <= ec against A.  Every weight then carries the same factor 2^dl
+  // relative to A while Aw stays, so O and the row sums need rescaling only when Aw moves,
+  // which happens when the lag would pass 30 - L (the bf8 byte (L - e_w) << 2 must stay a
+  // normal number) and on the first tile; with flush the lag stays 0 (its level-L byte is 0
+  // only unshifted).  The pre-pass kinds start their scores at -M and keep tb = G = 2^24.
+  float A = -__builtin_inff(), Aw = -__builtin_inff();
+  int dlag = 0;
+  const float lagmax = FLUSH ? 0.0f : (float)(30 - L);
   float tb = pot_g;
 
   // bf16 weights of 32-key block kb (exact / K-interval), as in the bf16 kernel
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
           uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
           const int key0 = kt * BN + kb * 32 + acc_key(r, hh);
           const s16x2 ue = __builtin_bit_cast(s16x2, u[hp]);
-          const int e0 = -(int)ue[0], e1 = -(int)ue[1];
+          const int e0 = -(int)ue[0] + dlag, e1 = -(int)ue[1] + dlag;  // against the running anchor
           if (key0 < N) dst[key0] = key0 > lim ? 255u : (FLUSH && e0 == L) ? 254u : (uint8_t)e0;
           if (key0 + 1 < N) dst[key0 + 1] = key0 + 1 > lim ? 255u : (FLUSH && e1 == L) ? 254u : (uint8_t)e1;
         }
@@ -469,11 +476,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     }
   };
 
-  // Single-pass PoT: fold the maximum of the next tile into the anchor before its weights are
-  // formed; when A rises by dA, O and the row sums, whose weights were formed against the old
-  // anchor, are scaled by 2^-dA (exact).  The row-sum MMA leaves the sum of query q(l) in lane
-  // l (q = l, l-16, l-16, l-32 for the four 16-lane groups; see the epilogue), whose factor
-  // is fetched from lane q(l).
+  // Single-pass PoT: fold the maximum of the next tile into the anchor A before its weights
+  // are formed; when the weight anchor Aw has to move (see above), O and the row sums, formed
+  // against the old Aw, are scaled by 2^(Aw_old - Aw) (exact).  The row-sum MMA leaves the sum
+  // of query q(l) in lane l (q = l, l-16, l-16, l-32 for the four 16-lane groups; see the
+  // epilogue), whose factor is fetched from lane q(l).
   auto run_anchor = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], int kt, bool masked) __attribute__((always_inline)) {
     float tm = -__builtin_inff();
 #pragma unroll
@@ -482,15 +489,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       for (int r = 0; r < 16; ++r)
         tm = fmaxf(tm, (!masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : -__builtin_inff());
     const float An = fmaxf(A, __builtin_ceilf(half_max(tm) * rc.c));
-    if (__builtin_amdgcn_ballot_w64(An > A)) {
-      const float alpha = An > A ? (A > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(A - An)) : 0.0f) : 1.0f;
+    if (__builtin_amdgcn_ballot_w64(An - Aw > lagmax)) {  // Aw = -inf before the first tile
+      const bool move = An - Aw > lagmax;
+      const float alpha = move ? (Aw > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(Aw - An)) : 0.0f) : 1.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       const int ql = lane < 16 ? lane : (lane < 48 ? lane - 16 : lane - 32);
       rs *= bitsf(__builtin_amdgcn_ds_bpermute(4 * ql, (int)fbits(alpha)));
-      A = An;
-      tb = pot_g - An;
+      Aw = move ? An : Aw;
+      tb = pot_g - Aw;
     }
+    A = An;
+    dlag = (int)(A - Aw);
+    pot_clip = 0x00010001u * (uint32_t)(uint16_t)(dlag - ec);
+    pot_lo = pot_bits - ec + dlag;
   };
 
   // ---- main loop --------------------------------------------------------------
@@ -655,7 +667,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   if (hh == 0) {
     const size_t ri = (size_t)bh * N + row;
     if (a.row_max) a.row_max[ri] = RUN ? A * 0.69314718055994531f : M * a.sc;  // single pass: A ln 2
-    if (a.row_sum) a.row_sum[ri] = PV8 ? __builtin_ldexpf(lt, 15 - L) : lt;  // PoT P carries 2^(L-15)
+    // PoT P carries 2^(L-15) (and, single pass, 2^dlag against the final anchor)
+    if (a.row_sum) a.row_sum[ri] = PV8 ? __builtin_ldexpf(lt, 15 - L - dlag) : lt;
     if (a.row_lo) a.row_lo[ri] = ((wk_kint(WK) && a.window_calib) || wk_support(WK)) ? M * a.sc - a.window : MN * a.sc;
   }
 #endif
