@@ -219,12 +219,12 @@ def board_energy(fn, seconds):
 
 
 def energy_run(args):
-    """Board energy per forward, Rowmax-PoT against the same kernel with exact exp and the online
-    control, on the causal 16K GQA workload (B 1, H 64, Hkv 8, N 16384, d 128, bf16) and on the
-    causal fp8 8K workload.  Board power drifts as the card warms, so the kinds alternate over
+    """Board energy per forward, Rowmax-PoT against the same kernel with exact exp, the online
+    control and the single-pass PoT, on the causal 16K GQA workload (B 1, H 64, Hkv 8, N 16384,
+    d 128, bf16) and on the causal fp8 8K workload.  Board power drifts as the card warms, so the kinds alternate over
     `--energy-rounds` rounds and the means are reported."""
     kinds = (("pot16", {"kind": "pot", "levels": 16}), ("exact_anchored", {"kind": "exact_anchored"}),
-             ("exact_online", {"kind": "exact"}))
+             ("exact_online", {"kind": "exact"}), ("pot16_single_pass", {"kind": "pot_running", "levels": 16}))
     rec = {"metric": "board energy per attention forward (J), amdsmi energy accumulator",
            "seconds_per_measurement": args.energy_seconds, "rounds": args.energy_rounds, "workloads": {}}
     for wname in ("gqa16k", "fp8_8k"):
@@ -248,6 +248,7 @@ def energy_run(args):
             w["ms_per_call"] = {n: float(np.mean([m["ms_per_call"] for m in ms])) for n, ms in runs.items()}
             w["pot_energy_vs_exact_anchored"] = mean["pot16"] / mean["exact_anchored"]
             w["pot_energy_vs_exact_online"] = mean["pot16"] / mean["exact_online"]
+            w["single_pass_energy_vs_exact_online"] = mean["pot16_single_pass"] / mean["exact_online"]
         rec["workloads"][wname] = w
         del x, dev_t, out
         torch.cuda.empty_cache()

@@ -45,6 +45,14 @@ def test_pot2k_sink(var):
     gc.run_parity(wl, var, heads=[(0, 0), (2, 17), (3, 31)], x=x)
 
 
+@pytest.mark.parametrize("var", [gc.POTR8, gc.POTR16], ids=gc.name)
+def test_gqa16k_sampled(var):
+    # long-context GQA 64/8 at 16K (logit std 4): seeded windows of three heads
+    wl = qin.WORKLOADS["gqa16k"]
+    x = qin.make_inputs(wl)
+    gc.run_parity(wl, var, heads=[(0, 0), (0, 9), (0, 63)], windows=gc.sample_windows(wl.N, n=4, seed=5), x=x)
+
+
 @pytest.fixture(scope="module")
 def fp8_8k():
     wl = qin.WORKLOADS["fp8_8k"]
