@@ -398,7 +398,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the kernel runs on one GPU's share of heads and needs no "
-              "collective; multi-GPU runs are not part of this build.", file=sys.stderr)
+              "collective; the benchmark has no multi-GPU mode.", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -64,7 +64,7 @@ typedef enum {
   QSA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                        */
   QSA_ERR_SHAPE = 2,       /* B, H, Hkv or N out of range, H % Hkv != 0, ...    */
   QSA_ERR_PARAM = 3,       /* k_levels, window, scale or descale out of range   */
-  QSA_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement     */
+  QSA_ERR_UNSUPPORTED = 4, /* a valid request the library does not implement    */
   QSA_ERR_HIP = 5          /* the HIP runtime reported an error at launch       */
 } qsa_status;
 

@@ -19,9 +19,9 @@
 //     active, so hard rounding gets dw/ds = w and the calibration term dw/dDelta = w (y - l).
 //   4 as 3 with the extrema detached.
 //
-// A correctness path like the float32 forward, not a tuned one: four lanes per query row or
-// key (lane u of a quad holds dimensions u, u+4, ..., so quads read LDS without bank
-// conflicts), fp32 FMAs, 64-row or 64-key tiles staged in LDS.  Three launches on the caller's
+// A float32 path on the vector ALU: four lanes per query row or key (lane u of a quad holds
+// four groups of four consecutive dimensions, see dim_of), fp32 FMAs, 64-row or 64-key tiles
+// staged in LDS and read as 16-byte vectors.  Three launches on the caller's
 // stream:
 //   bwd_rows  per query row, two passes over its keys: the extrema and their keys; then l, D
 //             and (attached modes) the gradients of m and lo, parked in the first 8 floats
@@ -51,13 +51,37 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-// x . row for the quad: lane u multiplies dimensions u, u+4, ... then the quad adds up
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Dimension held in register k of lane u of a quad: groups of four consecutive dimensions,
+// 16k' + 4u .. 16k' + 4u + 3 for k = 4k' .. 4k' + 3, so a lane reads a 16-byte LDS vector per
+// four FMAs and the four lanes of a quad cover 16 consecutive words (no bank conflicts; every
+// quad of a wave reads the same words, a broadcast).
+__device__ __forceinline__ int dim_of(int k, int u) { return 16 * (k >> 2) + 4 * u + (k & 3); }
+
+// x . row for the quad: four partial sums (one per vector component, four FMA chains in
+// flight), then the quad adds up
 template <int D>
 __device__ __forceinline__ float qdot(const float* row, const float (&x)[D / 4], int u) {
-  float p = 0.0f;
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int k = 0; k < D / 4; ++k) p = fmaf(x[k], row[4 * k + u], p);
-  return quad_sum(p);
+  for (int k4 = 0; k4 < D / 16; ++k4) {
+    const f4 r = *(const f4*)(row + 16 * k4 + 4 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fmaf(x[4 * k4 + i], r[i], p[i]);
+  }
+  return quad_sum((p[0] + p[1]) + (p[2] + p[3]));
+}
+
+// acc += a * row (the quad's dimensions of one LDS row)
+template <int D>
+__device__ __forceinline__ void qaxpy(float a, const float* row, float (&acc)[D / 4], int u) {
+#pragma unroll
+  for (int k4 = 0; k4 < D / 16; ++k4) {
+    const f4 r = *(const f4*)(row + 16 * k4 + 4 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 * k4 + i] = fmaf(a, r[i], acc[4 * k4 + i]);
+  }
 }
 
 // Gradient modes (the values of BwdArgs::mode)
@@ -151,8 +175,8 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   float q[DL], g[DL];
 #pragma unroll
   for (int k = 0; k < DL; ++k) {
-    q[k] = row < N ? ld(Qg + (size_t)row * D + 4 * k + u) : 0.0f;
-    g[k] = row < N ? ld(Gg + (size_t)row * D + 4 * k + u) : 0.0f;
+    q[k] = row < N ? ld(Qg + (size_t)row * D + dim_of(k, u)) : 0.0f;
+    g[k] = row < N ? ld(Gg + (size_t)row * D + dim_of(k, u)) : 0.0f;
   }
   const int kt_end = f.causal ? ((min(qt * TB + TB, N) - 1) / TB + 1) : (N + TB - 1) / TB;
   const int lim = row < N ? (f.causal ? row : N - 1) : -1;  // last key this row sees
@@ -170,6 +194,7 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
     __syncthreads();
     load_tile(Ks, Kg, kt);
     __syncthreads();
+#pragma unroll 4
     for (int j = 0; j < TB; ++j) {
       const int key = kt * TB + j;
       const float s = qdot<D>(Ks + j * D, q, u);
@@ -195,6 +220,7 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
     load_tile(Ks, Kg, kt);
     load_tile(Vs, Vg, kt);
     __syncthreads();
+#pragma unroll 4
     for (int j = 0; j < TB; ++j) {
       const float s = qdot<D>(Ks + j * D, q, u);
       const float dp = qdot<D>(Vs + j * D, g, u);
@@ -267,8 +293,8 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
   float kk[DL], vv[DL], dk[DL], dv[DL];
 #pragma unroll
   for (int k = 0; k < DL; ++k) {
-    kk[k] = key < N ? ld(Kg + (size_t)key * D + 4 * k + u) : 0.0f;
-    vv[k] = key < N ? ld(Vg + (size_t)key * D + 4 * k + u) : 0.0f;
+    kk[k] = key < N ? ld(Kg + (size_t)key * D + dim_of(k, u)) : 0.0f;
+    vv[k] = key < N ? ld(Vg + (size_t)key * D + dim_of(k, u)) : 0.0f;
     dk[k] = dv[k] = 0.0f;
   }
   const bool minmax = wk_kint(WK) && !f.window_calib;
@@ -298,6 +324,7 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
         }
       }
       __syncthreads();
+#pragma unroll 4
       for (int r = 0; r < TB; ++r) {
         const int i = qt * TB + r;
         if (i >= N) break;
@@ -311,12 +338,8 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
           const float dsc = wk_kint(WK) ? grid_step(f, pk[0], pk[1]) : 1.0f;
           const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, l, pk[3], pk[4], pk[5],
                                       __builtin_bit_cast(int, pk[6]), __builtin_bit_cast(int, pk[7]), dsc, minmax);
-          const float p = w / l;
-#pragma unroll
-          for (int k = 0; k < DL; ++k) {
-            dv[k] = fmaf(p, Gs[r * D + 4 * k + u], dv[k]);
-            dk[k] = fmaf(ds, Qs[r * D + 4 * k + u], dk[k]);
-          }
+          qaxpy<D>(w / l, Gs + r * D, dv, u);
+          qaxpy<D>(ds, Qs + r * D, dk, u);
         }
       }
     }
@@ -326,8 +349,8 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
     float* dVg = a.dv + ((size_t)(b * f.Hkv + kvh) * N + key) * D;
 #pragma unroll
     for (int k = 0; k < DL; ++k) {
-      dKg[4 * k + u] = f.sc * dk[k];
-      dVg[4 * k + u] = dv[k];
+      dKg[dim_of(k, u)] = f.sc * dk[k];
+      dVg[dim_of(k, u)] = dv[k];
     }
   }
 }
@@ -358,8 +381,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
   float pk[NPARK];
 #pragma unroll
   for (int k = 0; k < DL; ++k) {
-    q[k] = row < N ? ld(Qg + (size_t)row * D + 4 * k + u) : 0.0f;
-    g[k] = row < N ? ld(Gg + (size_t)row * D + 4 * k + u) : 0.0f;
+    q[k] = row < N ? ld(Qg + (size_t)row * D + dim_of(k, u)) : 0.0f;
+    g[k] = row < N ? ld(Gg + (size_t)row * D + dim_of(k, u)) : 0.0f;
     dq[k] = 0.0f;
   }
 #pragma unroll
@@ -381,6 +404,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
     load_tile(Ks, Kg, kt);
     load_tile(Vs, Vg, kt);
     __syncthreads();
+#pragma unroll 4
     for (int j = 0; j < TB; ++j) {
       const int key = kt * TB + j;
       const float s = qdot<D>(Ks + j * D, q, u);
@@ -389,14 +413,13 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
         const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
         const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, pk[2], pk[3], pk[4], pk[5], amax, amin,
                                     dsc, minmax);
-#pragma unroll
-        for (int k = 0; k < DL; ++k) dq[k] = fmaf(ds, Ks[j * D + 4 * k + u], dq[k]);
+        qaxpy<D>(ds, Ks + j * D, dq, u);
       }
     }
   }
   if (row < N) {
 #pragma unroll
-    for (int k = 0; k < DL; ++k) dQg[4 * k + u] = f.sc * dq[k];
+    for (int k = 0; k < DL; ++k) dQg[dim_of(k, u)] = f.sc * dq[k];
   }
 }
 
