@@ -45,9 +45,11 @@ __device__ __forceinline__ float ld(const T* p) {
   return (float)*p;
 }
 
+// Sum over the four lanes of a quad with DPP lane permutes (quad_perm 1,0,3,2 then 2,3,0,1):
+// every lane ends with (x0 + x1) + (x2 + x3), with no LDS round trip.
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
+  x += bitsf((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(x), 0xB1, 0xF, 0xF, false));
+  x += bitsf((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(x), 0x4E, 0xF, 0xF, false));
   return x;
 }
 
@@ -84,6 +86,10 @@ __device__ __forceinline__ void qaxpy(float a, const float* row, float (&acc)[D 
   }
 }
 
+struct GridD {
+  float dsc, idsc, ik, pad;
+};
+
 // Gradient modes (the values of BwdArgs::mode)
 constexpr int G_STE_POST = 0, G_EXACT = 1, G_EXACT_DET = 2, G_STE_PRE = 3, G_STE_PRE_DET = 4;
 __device__ __forceinline__ bool g_ste(int mode) { return mode == G_STE_PRE || mode == G_STE_PRE_DET; }
@@ -96,7 +102,7 @@ __device__ __forceinline__ bool g_attached(int mode) { return mode == G_EXACT ||
 // and on a min-max grid every visible key is inside (its arg-min sits on y = K up to rounding).
 template <int WK>
 __device__ __forceinline__ void partials(float acc, float w, const RowC& rc, const unsigned char* Tb, int K,
-                                         float dsc, bool minmax, bool ste, float& gs, float& cm, float& clo) {
+                                         const GridD& gd, bool minmax, bool ste, float& gs, float& cm, float& clo) {
   gs = cm = clo = 0.0f;
   if (WK == WK_EXACT || WK == WK_EXACT_ANCH || WK == WK_TRUNC) {  // w = exp(s - m) where kept
     gs = w;
@@ -136,19 +142,26 @@ __device__ __forceinline__ void partials(float acc, float w, const RowC& rc, con
       const float lf = fminf(r, Kf);
       const float tl = *(const float*)(Tb + ((((uint32_t)(int32_t)lf) << SHB) + rc.tab));
       dwdD = -lf * tl;
-      if (ste && r <= Kf) dwdy = -dsc * w;  // T_l = exp(-l Delta) with l := y
+      if (ste && r <= Kf) dwdy = -gd.dsc * w;  // T_l = exp(-l Delta) with l := y
     }
   }
-  const float inv = 1.0f / dsc;
+  const float inv = gd.idsc;
   gs = -dwdy * inv;
   const float dD = dwdD - dwdy * y * inv;  // total dw/dDelta with y moving with Delta
-  cm = dwdy * inv + (minmax ? dD / Kf : 0.0f);
-  clo = minmax ? -dD / Kf : 0.0f;
+  cm = dwdy * inv + (minmax ? dD * gd.ik : 0.0f);
+  clo = minmax ? -dD * gd.ik : 0.0f;
 }
 
-// Grid step in score units (K-interval), from the row extrema in raw units.
-__device__ __forceinline__ float grid_step(const FwdArgs& f, float M, float MN) {
-  return f.window_calib ? f.window / (float)f.levels : (M - MN) * f.sc / (float)f.levels;
+// Per-row grid constants of the K-interval derivatives (other kinds: unused ones): the grid
+// step Delta in score units, its reciprocal and 1/K, computed once per row so that no
+// element pays a division.
+__device__ __forceinline__ GridD grid_d(const FwdArgs& f, float M, float MN) {
+  GridD g;
+  g.dsc = f.window_calib ? f.window / (float)f.levels : (M - MN) * f.sc / (float)f.levels;
+  g.idsc = 1.0f / g.dsc;
+  g.ik = 1.0f / (float)f.levels;
+  g.pad = 0.0f;
+  return g;
 }
 
 template <typename T, int D, int WK>
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   }
   if (row >= N) M = MN = 0.0f;
   const RowC rc = make_row<WK, SHB>(f, M, MN, rl, Tb, u, 4);
-  const float dsc = wk_kint(WK) ? grid_step(f, M, MN) : 1.0f;
+  const GridD gd = grid_d(f, M, MN);
   const bool minmax = wk_kint(WK) && !f.window_calib;
 
   // l, D = sum_j P_ij dP_ij (= dO_i . O_i) and, with the extrema attached, the gradients of m
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
         wdp = fmaf(w, dp, wdp);
         if (calib) {
           float gs, cm, clo;
-          partials<WK>(s, w, rc, Tb, f.levels, dsc, minmax, g_ste(a.mode), gs, cm, clo);
+          partials<WK>(s, w, rc, Tb, f.levels, gd, minmax, g_ste(a.mode), gs, cm, clo);
           pm = fmaf(dp, cm, pm);
           sm += cm;
           plo = fmaf(dp, clo, plo);
@@ -258,12 +271,12 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
 // dS_ij from the weight, the row constants and dP_ij (modes as in the file header)
 template <int WK>
 __device__ __forceinline__ float dscore(int mode, float s, float w, float dp, int key, const RowC& rc,
-                                        const unsigned char* Tb, const FwdArgs& f, float l, float Dr, float dm,
-                                        float dlo, int amax, int amin, float dsc, bool minmax) {
-  if (mode == G_STE_POST) return (w / l) * (dp - Dr);
+                                        const unsigned char* Tb, const FwdArgs& f, float il, float Dr, float dm,
+                                        float dlo, int amax, int amin, const GridD& gd, bool minmax) {
+  if (mode == G_STE_POST) return (w * il) * (dp - Dr);  // il = 1 / l
   float gs, cm, clo;
-  partials<WK>(s, w, rc, Tb, f.levels, dsc, minmax, g_ste(mode), gs, cm, clo);
-  float ds = (dp - Dr) / l * gs;
+  partials<WK>(s, w, rc, Tb, f.levels, gd, minmax, g_ste(mode), gs, cm, clo);
+  float ds = (dp - Dr) * il * gs;
   if (g_attached(mode)) {
     if (key == amax) ds += dm;
     if (key == amin && minmax) ds += dlo;
@@ -278,9 +291,10 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* Qs = (float*)smem;
   float* Gs = Qs + TB * D;
-  float* Rp = Gs + TB * D;                               // [TB][NPARK] parked row constants
+  float* Rp = Gs + TB * D;                               // [TB][NPARK] parked row constants (1/l for l)
   RowC* Rc = (RowC*)(Rp + TB * NPARK);                   // [TB] row constants
-  unsigned char* Tb = (unsigned char*)(Rc + TB);
+  GridD* Rg = (GridD*)(Rc + TB);                         // [TB] grid constants of the derivatives
+  unsigned char* Tb = (unsigned char*)(Rg + TB);
 
   const int tid = threadIdx.x, kl = tid >> 2, u = tid & 3;
   const int N = f.N, nt = (N + TB - 1) / TB;
@@ -320,7 +334,9 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
         if (u == 0) {
 #pragma unroll
           for (int c = 0; c < NPARK; ++c) Rp[kl * NPARK + c] = pk[c];
+          Rp[kl * NPARK + 2] = 1.0f / pk[2];  // l >= 1 on a row (its maximum weighs 1); unused past N
           Rc[kl] = rc;
+          Rg[kl] = grid_d(f, pk[0], pk[1]);
         }
       }
       __syncthreads();
@@ -334,11 +350,10 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
           const RowC rc = Rc[r];
           const float* pk = Rp + r * NPARK;
           const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
-          const float l = pk[2];
-          const float dsc = wk_kint(WK) ? grid_step(f, pk[0], pk[1]) : 1.0f;
-          const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, l, pk[3], pk[4], pk[5],
-                                      __builtin_bit_cast(int, pk[6]), __builtin_bit_cast(int, pk[7]), dsc, minmax);
-          qaxpy<D>(w / l, Gs + r * D, dv, u);
+          const float il = pk[2];
+          const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, il, pk[3], pk[4], pk[5],
+                                      __builtin_bit_cast(int, pk[6]), __builtin_bit_cast(int, pk[7]), Rg[r], minmax);
+          qaxpy<D>(w * il, Gs + r * D, dv, u);
           qaxpy<D>(ds, Qs + r * D, dk, u);
         }
       }
@@ -388,7 +403,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < NPARK; ++c) pk[c] = row < N ? dQg[c] : 0.0f;  // before the row is overwritten
   const RowC rc = make_row<WK, SHB>(f, pk[0], pk[1], rl, Tb, u, 4);
-  const float dsc = wk_kint(WK) ? grid_step(f, pk[0], pk[1]) : 1.0f;
+  const GridD gd = grid_d(f, pk[0], pk[1]);
+  const float il = 1.0f / pk[2];  // unused past N (no visible key)
   const bool minmax = wk_kint(WK) && !f.window_calib;
   const int amax = __builtin_bit_cast(int, pk[6]), amin = __builtin_bit_cast(int, pk[7]);
   const int kt_end = f.causal ? ((min(qt * TB + TB, N) - 1) / TB + 1) : (N + TB - 1) / TB;
@@ -411,8 +427,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
       const float dp = qdot<D>(Vs + j * D, g, u);
       if (key <= lim) {
         const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
-        const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, pk[2], pk[3], pk[4], pk[5], amax, amin,
-                                    dsc, minmax);
+        const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, il, pk[3], pk[4], pk[5], amax, amin, gd,
+                                    minmax);
         qaxpy<D>(ds, Ks + j * D, dq, u);
       }
     }
@@ -430,7 +446,8 @@ hipError_t launch_typed(const BwdArgs& a0, hipStream_t st) {
   a.f.total_blocks = a.f.B * a.f.H * a.f.n_qtiles;
   const size_t tab = table_bytes(WK, TB, a.f.levels);
   const size_t lds_rows = 2 * (size_t)TB * D * 4 + tab;
-  const size_t lds_keys = 2 * (size_t)TB * D * 4 + (size_t)TB * NPARK * 4 + (size_t)TB * sizeof(RowC) + tab;
+  const size_t lds_keys =
+      2 * (size_t)TB * D * 4 + (size_t)TB * NPARK * 4 + (size_t)TB * sizeof(RowC) + (size_t)TB * sizeof(GridD) + tab;
   const void* ks[3] = {(const void*)bwd_rows<T, D, WK>, (const void*)bwd_keys<T, D, WK>, (const void*)bwd_dq<T, D, WK>};
   const size_t lds[3] = {lds_rows, lds_keys, lds_rows};
   for (int i = 0; i < 3; ++i)
