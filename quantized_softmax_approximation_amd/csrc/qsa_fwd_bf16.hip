@@ -190,24 +190,32 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     f32x16 s[2];
     if (wlast >= 0) qk(0, s, zero16);
     __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-    for (int t = 0; t < T; ++t) {
+    // tiles before the wave's last (no masking), then the last tile and the iterations in
+    // which the wave only issues its share of the other waves' loads: two loops, so that the
+    // masking code stays out of the first (every wave still passes T barriers)
+    int t = 0;
+    for (; t < wlast; ++t) {
       if (t + 2 < T) load_k(t + 2, t & 1);  // buffer t&1 was last read in iteration t-1
-      if (t < wlast) {
-        f32x16 sn[2];
-        qk((t + 1) & 1, sn, zero16);
+      f32x16 sn[2];
+      qk((t + 1) & 1, sn, zero16);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
+      if (tmin) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
-        if (tmin) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
-        }
-        s[0] = sn[0];
-        s[1] = sn[1];
-      } else if (t == wlast) {
+          for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+      }
+      s[0] = sn[0];
+      s[1] = sn[1];
+      loads_done();
+      __syncthreads();
+    }
+    for (; t < T; ++t) {
+      if (t + 2 < T) load_k(t + 2, t & 1);
+      if (t == wlast) {
         f32x16 sm[2] = {s[0], s[1]};
         if (last_masked) mask_fill(sm, t, -__builtin_inff());
 #pragma unroll
@@ -411,23 +419,32 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   f32x16 s[2];
   if (wlast >= 0) qk(0, s, init16);
   __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-  for (int t = 0; t < T; ++t) {
+  // Tiles before the wave's last (unmasked), then its last tile and the iterations in which it
+  // only issues its share of the other waves' loads: two loops, so that the masking code stays
+  // out of the first (merged into one body it ran on every tile); every wave passes T barriers.
+  int t = 0;
+  for (; t < wlast; ++t) {
     if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
     if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
-    if (t < wlast) {
-      // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
-      const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
-      if (WK == WK_EXACT) online_max(s, o, l);
-      if (RUN) run_anchor(s, o, l, t, false);
-      u32x4 P[2];
-      weights(s[0], 0, P, l, t, false);
-      pv1(t & 1, 0, P, o);
-      const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
-      weights(s[1], 1, P, l, t, false);
-      pv1(t & 1, 1, P, o);
-      s[0] = sn0;
-      s[1] = sn1;
-    } else if (t == wlast) {
+    // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
+    const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
+    if (WK == WK_EXACT) online_max(s, o, l);
+    if (RUN) run_anchor(s, o, l, t, false);
+    u32x4 P[2];
+    weights(s[0], 0, P, l, t, false);
+    pv1(t & 1, 0, P, o);
+    const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
+    weights(s[1], 1, P, l, t, false);
+    pv1(t & 1, 1, P, o);
+    s[0] = sn0;
+    s[1] = sn1;
+    loads_done();
+    __syncthreads();
+  }
+  for (; t < T; ++t) {
+    if (t + 2 < T) load_k(t + 2, t & 1);
+    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
+    if (t == wlast) {
       if (WK == WK_EXACT) {
         f32x16 sm[2] = {s[0], s[1]};
         if (last_masked) mask_fill(sm, t, -__builtin_inff());
