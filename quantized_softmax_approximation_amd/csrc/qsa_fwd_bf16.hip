@@ -422,24 +422,35 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   // Tiles before the wave's last (unmasked), then its last tile and the iterations in which it
   // only issues its share of the other waves' loads: two loops, so that the masking code stays
   // out of the first (merged into one body it ran on every tile); every wave passes T barriers.
-  int t = 0;
-  for (; t < wlast; ++t) {
+  // the scores of tile t+1 go to the other of two register sets, whose roles swap every
+  // iteration (unrolled by two), so no copy of 32 registers per tile
+  auto steady = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) __attribute__((always_inline)) {
     if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
     if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
     // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
-    const f32x16 sn0 = qk1((t + 1) & 1, 0, init16);
-    if (WK == WK_EXACT) online_max(s, o, l);
-    if (RUN) run_anchor(s, o, l, t, false);
+    nxt[0] = qk1((t + 1) & 1, 0, init16);
+    if (WK == WK_EXACT) online_max(cur, o, l);
+    if (RUN) run_anchor(cur, o, l, t, false);
     u32x4 P[2];
-    weights(s[0], 0, P, l, t, false);
+    weights(cur[0], 0, P, l, t, false);
     pv1(t & 1, 0, P, o);
-    const f32x16 sn1 = qk1((t + 1) & 1, 1, init16);
-    weights(s[1], 1, P, l, t, false);
+    nxt[1] = qk1((t + 1) & 1, 1, init16);
+    weights(cur[1], 1, P, l, t, false);
     pv1(t & 1, 1, P, o);
-    s[0] = sn0;
-    s[1] = sn1;
     loads_done();
     __syncthreads();
+  };
+  f32x16 s2[2];
+  int t = 0;
+  for (; t + 1 < wlast; t += 2) {
+    steady(s, s2, t);
+    steady(s2, s, t + 1);
+  }
+  if (t < wlast) {
+    steady(s, s2, t);
+    s[0] = s2[0];
+    s[1] = s2[1];
+    ++t;
   }
   for (; t < T; ++t) {
     if (t + 2 < T) load_k(t + 2, t & 1);
