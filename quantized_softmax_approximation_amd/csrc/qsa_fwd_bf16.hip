@@ -193,25 +193,34 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     // tiles before the wave's last (no masking), then the last tile and the iterations in
     // which the wave only issues its share of the other waves' loads: two loops, so that the
     // masking code stays out of the first (every wave still passes T barriers)
-    int t = 0;
-    for (; t < wlast; ++t) {
+    // (unrolled by two with the score registers swapping roles, as in the main loop)
+    auto fold = [&](const f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) __attribute__((always_inline)) {
       if (t + 2 < T) load_k(t + 2, t & 1);  // buffer t&1 was last read in iteration t-1
-      f32x16 sn[2];
-      qk((t + 1) & 1, sn, zero16);
+      qk((t + 1) & 1, nxt, zero16);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) M = fmaxf(M, s[kb][r]);
+        for (int r = 0; r < 16; ++r) M = fmaxf(M, cur[kb][r]);
       if (tmin) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
+          for (int r = 0; r < 16; ++r) MN = fminf(MN, cur[kb][r]);
       }
-      s[0] = sn[0];
-      s[1] = sn[1];
       loads_done();
       __syncthreads();
+    };
+    f32x16 s2[2];
+    int t = 0;
+    for (; t + 1 < wlast; t += 2) {
+      fold(s, s2, t);
+      fold(s2, s, t + 1);
+    }
+    if (t < wlast) {
+      fold(s, s2, t);
+      s[0] = s2[0];
+      s[1] = s2[1];
+      ++t;
     }
     for (; t < T; ++t) {
       if (t + 2 < T) load_k(t + 2, t & 1);
