@@ -21,8 +21,8 @@
 //
 // A float32 path on the vector ALU: four lanes per query row or key (lane u of a quad holds
 // four groups of four consecutive dimensions, see dim_of), fp32 FMAs, 64-row or 64-key tiles
-// staged in LDS and read as 16-byte vectors.  Three launches on the caller's
-// stream:
+// staged in LDS and read as 16-byte vectors, quad sums by DPP, per-row reciprocals instead of
+// per-element divisions.  Three launches on the caller's stream:
 //   bwd_rows  per query row, two passes over its keys: the extrema and their keys; then l, D
 //             and (attached modes) the gradients of m and lo, parked in the first 8 floats
 //             of the row's dQ;
@@ -86,6 +86,8 @@ __device__ __forceinline__ void qaxpy(float a, const float* row, float (&acc)[D 
   }
 }
 
+// Per-row constants of the K-interval derivatives: the grid step Delta in score units, its
+// reciprocal and 1/K (see grid_d).
 struct GridD {
   float dsc, idsc, ik, pad;
 };
@@ -96,8 +98,8 @@ __device__ __forceinline__ bool g_ste(int mode) { return mode == G_STE_PRE || mo
 __device__ __forceinline__ bool g_attached(int mode) { return mode == G_EXACT || mode == G_STE_PRE; }
 
 // Per-element derivatives of the weight for the exact and pre-normalisation surrogate modes:
-// gs = dw/ds (direct, score units), cm = dw/dm, clo = dw/dlo.  dsc: grid step Delta in score
-// units (K-interval).  STE: the rounding of the grid coordinate is passed straight through
+// gs = dw/ds (direct, score units), cm = dw/dm, clo = dw/dlo.  gd: the row's grid step, its
+// reciprocal and 1/K (K-interval).  STE: the rounding of the grid coordinate is passed straight through
 // where the clip to the last level is not active.  At y = K the last interval's slope applies,
 // and on a min-max grid every visible key is inside (its arg-min sits on y = K up to rounding).
 template <int WK>
