@@ -41,6 +41,7 @@ struct RowC {
   float mc;     // M * c
   uint32_t tab; // K-interval: byte offset of this row's column in the LDS table
   float cut;    // support kinds: the support edge W log2(e) in y units
+  float step;   // K-interval: -Delta log2(e) (score units), so T_l = 2^(l step)
 };
 
 // Table layout (K-interval): entry l of local row r sits at byte
@@ -166,15 +167,18 @@ template <> struct Weight<WK_TRUNC> : SupportW<false> {};
 template <> struct Weight<WK_UNIF> : SupportW<true> {};
 
 // Per-row constants from the pre-pass extrema (raw units) and, for
-// K-interval, the row's grid table written into LDS.  The K+1 table entries
-// are split between the `nsplit` lanes that share a row (this lane writes
-// entries part, part + nsplit, ...).
+// K-interval, the row's grid table written into LDS (unless `tab` is null:
+// the bf16 kernel evaluates T_l = 2^(l step) from the index with the same
+// instruction instead, which gives the same values without the table).  The
+// K+1 table entries are split between the `nsplit` lanes that share a row
+// (this lane writes entries part, part + nsplit, ...).
 template <int WK, int SH>
 __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, int row_local,
                                          unsigned char* tab, int part, int nsplit) {
   RowC rc;
   rc.tab = 0;
   rc.cut = a.window * kLog2e;
+  rc.step = 0.0f;
   if (!wk_kint(WK)) {
     rc.c = a.sc * kLog2e;
     rc.mc = M * rc.c;
@@ -192,9 +196,11 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
   }
   rc.mc = M * rc.c;
   const float step = -delta_s * kLog2e;
+  rc.step = step;
   constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH);
   constexpr int ROWS = (1 << SH) / 4;
   rc.tab = (uint32_t)row_local * (INTERP ? 8u : 4u);
+  if (tab == nullptr) return rc;
   for (int l = part; l <= K; l += nsplit) {
     const float t0 = __builtin_amdgcn_exp2f(step * (float)l);
     if (INTERP) {
@@ -206,6 +212,15 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
     }
   }
   return rc;
+}
+
+// K-interval interpolation without the table: (T_l, T_{l+1} - T_l) for the index fl = l (a
+// float), the entry the table would hold (at l = K the table's difference is 0, but there the
+// interpolation parameter is 0 as well, so the weight is the same).
+__device__ __forceinline__ float __attribute__((ext_vector_type(2))) kgrid_pair(float step, float fl) {
+  const float t0 = __builtin_amdgcn_exp2f(step * fl);
+  const float t1 = __builtin_amdgcn_exp2f(step * (fl + 1.0f));
+  return {t0, t1 - t0};
 }
 
 // Table bytes a workgroup of ROWS rows needs for weight kind WK.
