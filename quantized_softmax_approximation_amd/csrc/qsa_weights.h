@@ -232,11 +232,23 @@ __host__ __device__ inline size_t table_bytes(int wk, int rows, int K) {
 
 // Block index -> (batch*head, query tile).  Workgroups are dispatched round-
 // robin over the 8 XCDs (workgroup w runs on XCD w % 8); the remap gives each
-// XCD a contiguous range of logical tiles, so the query tiles of one head
-// share an XCD and its L2 while they sweep the same K/V.  Causal launches
-// take the longest (last) query tiles of each head first.
+// XCD a contiguous range of heads, so the query tiles of one head (and the
+// heads of one GQA group) share an XCD and its L2 while they sweep the same
+// K/V.  Causal launches, whose query tile t costs t + 1 key tiles, are ordered
+// longest first across all of the XCD's heads (list scheduling in decreasing
+// cost), so the last workgroups to start are the shortest; taking each head's
+// tiles in turn instead left one head's long tiles starting late (when the
+// row count per head is below what an XCD holds at once).  That needs B*H to
+// be a multiple of 8; otherwise the causal order is longest first per head.
 __device__ __forceinline__ void map_block(const FwdArgs& a, int& bh, int& qt) {
   const int L = blockIdx.x, T = a.total_blocks;
+  const int BH = a.B * a.H;
+  if (a.causal && (BH & 7) == 0) {
+    const int j = L % BH, t = L / BH;  // workgroup L runs on XCD L % 8 = j % 8
+    bh = (j & 7) * (BH >> 3) + (j >> 3);
+    qt = a.n_qtiles - 1 - t;
+    return;
+  }
   const int x = L & 7, slot = L >> 3;
   const int per = T >> 3, rem = T & 7;
   const int logical = x * per + (x < rem ? x : rem) + slot;
