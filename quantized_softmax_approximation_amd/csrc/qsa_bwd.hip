@@ -286,6 +286,26 @@ __device__ __forceinline__ float dscore(int mode, float s, float w, float dp, in
   return ds;
 }
 
+// Block index -> (batch * KV head, key tile) for bwd_keys, on the same principles as the
+// query-tile map of the forward: each XCD (workgroup w runs on XCD w % 8) takes a contiguous
+// range of KV heads, whose query heads' Q and dO it then reads through one L2; causal key tile
+// kt costs nt - kt query tiles, so causal launches go in decreasing cost (ascending kt) across
+// all of the XCD's KV heads when B * Hkv is a multiple of 8.
+__device__ __forceinline__ void map_key_block(const FwdArgs& f, int nt, int& bkv, int& kt) {
+  const int L = blockIdx.x, BKV = f.B * f.Hkv;
+  if (f.causal && (BKV & 7) == 0) {
+    const int j = L % BKV;
+    kt = L / BKV;
+    bkv = (j & 7) * (BKV >> 3) + (j >> 3);
+    return;
+  }
+  const int T = BKV * nt, x = L & 7, slot = L >> 3;
+  const int per = T >> 3, rem = T & 7;
+  const int logical = x * per + (x < rem ? x : rem) + slot;
+  bkv = logical / nt;
+  kt = logical - bkv * nt;
+}
+
 template <typename T, int D, int WK>
 __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
   const FwdArgs& f = a.f;
@@ -300,7 +320,8 @@ __global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
 
   const int tid = threadIdx.x, kl = tid >> 2, u = tid & 3;
   const int N = f.N, nt = (N + TB - 1) / TB;
-  const int kt = blockIdx.x % nt, bkv = blockIdx.x / nt;
+  int bkv, kt;
+  map_key_block(f, nt, bkv, kt);
   const int b = bkv / f.Hkv, kvh = bkv - b * f.Hkv;
   const int group = f.H / f.Hkv;
   const int key = kt * TB + kl;
