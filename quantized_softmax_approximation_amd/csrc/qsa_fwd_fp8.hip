@@ -562,14 +562,27 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
       lds_barrier();
     };
     // steady state: tiles t, t+1 and t+2 all hold visible keys, none needs masking
+    // Single pass: the wave holds a raised issue priority while it issues its MMAs, so that of
+    // the two waves on a SIMD the one with matrix work ready goes first (measured: -2 % for the
+    // single pass, +3.5 % for PoT with the pre-pass, which therefore runs without it).
+    auto prio_hi = [&]() __attribute__((always_inline)) {
+      if (RUN) __builtin_amdgcn_s_setprio(1);
+    };
+    auto prio_lo = [&]() __attribute__((always_inline)) {
+      if (RUN) __builtin_amdgcn_s_setprio(0);
+    };
     auto steady = [&](int b0, int b1, int b2) __attribute__((always_inline)) {
+      prio_hi();
       mma_pv8(va, P8c, o);
       read_v8(b1, va);
       prefetch_to(b0, b1);
       const f32x16 sn0 = qk1(b2, 0, init16);
+      prio_lo();
       if (RUN) run_anchor(s, o, t + 1, false);
       weights8(s, P8c, t + 1, false);
+      prio_hi();
       const f32x16 sn1 = qk1(b2, 1, init16);
+      prio_lo();
       s[0] = sn0;
       s[1] = sn1;
       wait_tiles();
