@@ -40,7 +40,7 @@ namespace {
 constexpr int NW = 4;    // waves per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int BM = 128;  // query rows per workgroup
-constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
+constexpr int SH = 9;    // log2(BM * 4): the row-constant template's table stride (no table is built here)
 #ifndef QSA_BF16_WAVES_PER_SIMD
 #define QSA_BF16_WAVES_PER_SIMD 2
 #endif
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   load_v(0, 0);
   if (T > 1) load_k(1, 1);
   loads_done();
-  __syncthreads();  // also publishes the K-interval tables
+  __syncthreads();
   f32x16 s[2];
   if (wlast >= 0) qk(0, s, init16);
   __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
@@ -516,7 +516,7 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   // No K-interval table: the weights evaluate T_l = 2^(l step) from the grid index (one
   // v_exp_f32 per element, interpolation two).  In bf16 that measured 25-33 % faster than the
   // per-element LDS gather from a per-row table, which also cost LDS space; the fp8 kernel,
-  // whose transcendental rate limits it, keeps the table.
+  // whose loop is bound by VALU issue, keeps the table (there the evaluated form was slower).
   const size_t lds = 2 * (size_t)BN * ((D / 8 + 1) + (D / 8 + 4)) * 16;
   const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true> : (const void*)fwd_bf16<D, WK, false>;
   if (lds > 65536) {
