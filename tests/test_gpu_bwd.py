@@ -147,6 +147,15 @@ def test_bwd_tiny_shapes():
                 _case(wl, var, grad)
 
 
+def test_bwd_causal_tile_order_ragged():
+    # B * Hkv a multiple of 8 under a causal mask takes the longest-first block order of all three
+    # launches; a ragged N puts a partial tile last in every head
+    wl = qin.custom("bwd_order", B=2, H=8, Hkv=4, N=150, d=64, dtype="bf16", causal=True, sigma_qk=1.5, seed=2121)
+    for var in (gc.EXACT, gc.KH4, gc.KI4W, gc.POT8):
+        for grad in ("ste_post", "ste_pre", "exact"):
+            _case(wl, var, grad)
+
+
 # GPT-2-small shaped pretraining attention (B 8, 12 heads, 1024 keys, d 64, bf16, causal): the
 # whole problem on the GPU, two batch entries compared in full.
 @pytest.mark.parametrize("var,grad", [(gc.KH4, "ste_pre"), (gc.KH4, "exact"), (gc.KI16W, "ste_post"),
