@@ -306,8 +306,17 @@ __device__ __forceinline__ void map_key_block(const FwdArgs& f, int nt, int& bkv
   kt = logical - bkv * nt;
 }
 
+// Waves per SIMD the register budget of bwd_keys is sized for: 4 at d = 64 (at most 128 VGPRs,
+// 12-40 bytes spilled; the GPT-2 shaped backward measured 5 % faster than at the 140 VGPRs and 3
+// waves the compiler picks unbounded), no bound otherwise (d = 128 spills kilobytes at 4, and the
+// interpolation kinds, which spill most at d = 64, measured 1 % slower with it).
+template <int D, int WK>
+constexpr int keys_waves() {
+  return (D == 64 && WK != WK_KI && WK != WK_KI_FLUSH) ? 4 : 1;
+}
+
 template <typename T, int D, int WK>
-__global__ __launch_bounds__(256) void bwd_keys(BwdArgs a) {
+__global__ __launch_bounds__(256, (keys_waves<D, WK>())) void bwd_keys(BwdArgs a) {
   const FwdArgs& f = a.f;
   constexpr int DL = D / 4;
   extern __shared__ __align__(16) unsigned char smem[];
