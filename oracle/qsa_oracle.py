@@ -146,7 +146,7 @@ def _check_kind(kind, levels, window, interp, flush):
 
 def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Optional[int] = None,
                 window: Optional[float] = None, interp: bool = False, flush: bool = False,
-                extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE):
+                extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE, anchors: Optional[np.ndarray] = None):
     """Weights for a block of score rows.
 
     S: (R, N) float64 scaled scores; visible: (R, N) bool, at least one True
@@ -157,7 +157,11 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
     columns of S are the keys in order (pot_running visits them in tiles of
     ``tile``).  ``extrema`` = (m, mn), each (R,),
     replaces the row maximum and minimum (the forward with the calibration held
-    fixed, whose derivative is the detached gradient).
+    fixed, whose derivative is the detached gradient).  ``anchors`` (pot_running
+    only), (R, number of tiles), replaces the anchor after each tile, which the
+    definition takes as ceil(running max of s log2 e): a tile maximum that lies on
+    an integer up to rounding may be rounded up either way by an implementation
+    in lower precision, and this lets a comparison weigh the other choice.
     """
     _check_kind(kind, levels, window, interp, flush)
     R, N = S.shape
@@ -197,6 +201,8 @@ def row_weights(S: np.ndarray, visible: np.ndarray, *, kind: str, levels: Option
         nt = (N + tile - 1) // tile
         tmax = np.stack([t[:, c * tile:(c + 1) * tile].max(axis=1) for c in range(nt)], axis=1)
         A = np.ceil(np.maximum.accumulate(tmax, axis=1))      # anchor after each tile (-inf before any key)
+        if anchors is not None:
+            A = np.asarray(anchors, dtype=np.float64).reshape(R, nt)
         Aj = np.repeat(A, tile, axis=1)[:, :N]                # the anchor a key's tile was weighed with
         Afin = A[:, -1]
         y = np.where(visible, Aj - np.where(visible, t, 0.0), np.nan)
@@ -280,11 +286,12 @@ def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Seq
               causal: bool = False, kind: str = "exact", levels: Optional[int] = None,
               window: Optional[float] = None, interp: bool = False, flush: bool = False,
               scale: Optional[float] = None, detail: bool = False, chunk: int = 512,
-              extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE):
+              extrema: Optional[tuple] = None, tile: int = ANCHOR_TILE, anchors: Optional[np.ndarray] = None):
     """One (batch, head) pair: qh (N, d), kh/vh (N, d) float64.
 
     ``rows`` selects query rows (default: all).  Returns dict with O (R, d),
     m, lo, l (R,) and, if ``detail``, w, idx, y (R, N) and delta (R,).
+    ``anchors`` (pot_running): per-tile anchors of the selected rows, (R, tiles).
     """
     Nq, d = qh.shape
     N = kh.shape[0]                                        # keys (equal to Nq in attention proper)
@@ -297,8 +304,9 @@ def head_rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, rows: Optional[Seq
         cols = np.arange(N)
         visible = (cols[None, :] <= r[:, None]) if causal else np.ones((len(r), N), dtype=bool)
         ext = None if extrema is None else (np.asarray(extrema[0])[r], np.asarray(extrema[1])[r])
+        anc = None if anchors is None else np.asarray(anchors)[c0:c0 + chunk]
         rw = row_weights(S, visible, kind=kind, levels=levels, window=window, interp=interp, flush=flush,
-                         extrema=ext, tile=tile)
+                         extrema=ext, tile=tile, anchors=anc)
         w = rw["w"]
         l = w.sum(axis=1)                                  # row sum of the approximate weights
         O = (w @ vh) / l[:, None]                          # normalise, then P.V

@@ -110,6 +110,9 @@ def weight_row(scores, visible, kind, levels=None, window=None, interp=False, fl
     lo = (m - window) if window is not None else mn
     step = (m - lo) / K
     grid_vals = [math.exp(-l * step) for l in range(K + 1)]
+    # A min-max grid ends at the row minimum, so no visible score lies below it: flushing
+    # applies to fixed windows only (a y a rounding step above K at the minimum stays in).
+    flush = flush and window is not None
     for s, ok in zip(scores, visible):
         if not ok:
             out.append(0.0)

@@ -122,6 +122,25 @@ def _check_out(t, shape, dtype, dev, name):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
 
 
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """Shapes, dtype, device and layout of the inputs; every kernel sizes its reads of K and V
+    from q's N and d, so a shorter k or v must be refused here, before any launch."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H(kv), N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError(f"k and v must be [B, Hkv, N, d] = {(B, Hkv, N, d)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float8_e4m3fn")
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    return B, H, N, d, Hkv, dev
+
+
 def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, kind: str = "exact",
                 levels: int = 0, window: Optional[float] = None, interp: bool = False, flush: bool = False,
                 scale: float = 0.0, q_descale: float = 0.0, k_descale: float = 0.0, v_descale: float = 0.0,
@@ -138,19 +157,7 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     written when given.  The call is asynchronous on `stream` (default: the
     current stream).
     """
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H(kv), N, d]")
-    B, H, N, d = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
-        raise ValueError(f"k and v must be [B, Hkv, N, d] = {(B, Hkv, N, d)}")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
-        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float8_e4m3fn")
-    dev = q.device
-    if dev.type != "cuda" or k.device != dev or v.device != dev:
-        raise ValueError("q, k, v must be on the same GPU")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d, Hkv, dev = _check_qkv(q, k, v)
     dt = _DT[q.dtype]
     odt = torch.float32 if dt == DT_F32 else torch.bfloat16
     if out is None:
@@ -178,23 +185,19 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, kind: str = "exact",
              levels: int = 0, window: Optional[float] = None, interp: bool = False, flush: bool = False,
              out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Attention forward through qsa_attn_fwd (scale 1/sqrt(d), descales 1)."""
+    """Attention forward through qsa_attn_fwd (scale 1/sqrt(d), descales 1).  Tensors as for
+    attn_fwd_ex (float32 or bfloat16; fp8 needs the descales of attn_fwd_ex)."""
     if q.dtype == torch.float8_e4m3fn:
         raise ValueError("fp8 inputs need per-tensor descales: use attn_fwd_ex")
-    B, H, N, d = q.shape
-    Hkv = k.shape[1]
-    if not (q.is_cuda and k.is_cuda and v.is_cuda and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous GPU tensors")
-    if q.dtype not in _DT or not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k, v must share one dtype among float32, bfloat16")
+    B, H, N, d, Hkv, dev = _check_qkv(q, k, v)
     dt = _DT[q.dtype]
     odt = torch.float32 if dt == DT_F32 else torch.bfloat16
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
-    _check_out(out, (B, H, N, d), odt, q.device, "out")
+        out = torch.empty((B, H, N, d), dtype=odt, device=dev)
+    _check_out(out, (B, H, N, d), odt, dev, "out")
     variant = variant_code(kind, interp=interp, window=window, flush=flush)
-    st = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
+    st = (stream or torch.cuda.current_stream(dev)).cuda_stream
+    with torch.cuda.device(dev):
         status = lib().qsa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(bool(causal)),
                                     variant, int(levels), float(window or 0.0), dt, ctypes.c_void_p(st))
     if status != OK:

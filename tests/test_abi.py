@@ -161,6 +161,21 @@ def test_binding_rejects_bad_tensors_on_host():
         qsa.attn_fwd_ex(q, q.double(), q)             # dtype mismatch
 
 
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_ex"])
+def test_binding_refuses_short_kv_before_launch(fn):
+    # the kernels size their K and V reads from q's N and d: a k or v with fewer keys, another
+    # head dimension or a missing axis must be refused by the shape check (it runs before the
+    # device check, so host tensors reach it without a GPU)
+    import torch
+    f = getattr(qsa, fn)
+    q = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16)
+    good = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    for bad_k, bad_v in ((q[:, :2, :32], good), (good, q[:, :2, :32]), (good[..., :32], good),
+                         (good[0], good), (torch.zeros(2, 2, 64, 64, dtype=torch.bfloat16), good)):
+        with pytest.raises(ValueError, match="k and v must be|must be 4-D"):
+            f(q, bad_k.contiguous(), bad_v.contiguous(), kind="pot", levels=8)
+
+
 def _bwd(ptrs=(1, 1, 1, 1, 1, 1, 1), grad=0, scale=0.0, **kw):
     a = dict(GOOD)
     a.update(kw)

@@ -39,7 +39,7 @@ def test_tiny_fp32(var):
 # ---------------------------------------------------------------- GPT-2 shaped (bf16, causal)
 
 GPT2_VARS = [gc.EXACT, gc.POT8, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KH16W, gc.KI4W, gc.KI16W, gc.TRUNC2,
-             gc.UNIF2]
+             gc.UNIF2, gc.KH4F, gc.KI4F]
 
 
 @pytest.fixture(scope="module")
@@ -80,8 +80,8 @@ def gqa16k():
     return wl, x, gc.to_gpu(x), gc.decoded(x)
 
 
-@pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT16, gc.KH4, gc.KH16, gc.KI16, gc.KH4W,
-                                 gc.KH16W, gc.KI4W, gc.TRUNC2, gc.UNIF2], ids=gc.name)
+@pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT16, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W,
+                                 gc.KH16W, gc.KI4W, gc.KI16W, gc.TRUNC2, gc.UNIF2], ids=gc.name)
 def test_gqa16k_sampled(gqa16k, var):
     wl, x, dev_t, f64 = gqa16k
     heads = [(0, 0), (0, 9), (0, 63)]
@@ -100,15 +100,36 @@ def test_ragged(N, d, causal):
     wl = qin.custom(f"ragged{N}", B=2, H=4, Hkv=2, N=N, d=d, dtype="bf16", causal=causal, sigma_qk=1.5, seed=N + d)
     x = qin.make_inputs(wl)
     dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
-    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2, gc.UNIF2):
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2, gc.UNIF2,
+                gc.KH4F):
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
+
+
+# ---------------------------------------------------------------- the 8K shape in bf16 (the stricter 60 % reading)
+
+@pytest.fixture(scope="module")
+def bf16_8k():
+    wl = qin.WORKLOADS["fp8_8k"].replace(dtype="bf16")
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("var", [gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT8, gc.POTR16, gc.KH16W, gc.KI16W, gc.KH16,
+                                 gc.TRUNC2], ids=gc.name)
+def test_bf16_8k_sampled(bf16_8k, var, causal):
+    # the launch bench.py times at B 1, H 32, N 8192, d 128 with bf16 inputs; seeded 64-row windows
+    # (always the first and the last 64 rows) of three heads
+    wl, x, dev_t, f64 = bf16_8k
+    gc.run_parity(wl.replace(causal=causal), var, heads=[(0, 0), (0, 13), (0, 31)],
+                  windows=gc.sample_windows(wl.N, n=3, seed=12), x=x, dev_t=dev_t, f64=f64)
 
 
 @pytest.mark.parametrize("N", [1, 5, 64, 100])
 def test_ragged_fp32(N):
     wl = qin.custom(f"f32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
     x = qin.make_inputs(wl)
-    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W, gc.TRUNC2, gc.UNIF2):
+    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W, gc.TRUNC2, gc.UNIF2, gc.KH4F):
         gc.run_parity(wl, var, x=x, verbose=False)
 
 
@@ -263,5 +284,5 @@ def test_fp8_ragged(N, d, causal):
     x = qin.make_inputs(wl)
     dev_t, f64 = gc.to_gpu(x), gc.decoded(x)
     for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2,
-                gc.UNIF2):
+                gc.UNIF2, gc.KH4F):
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)

@@ -52,6 +52,8 @@ MUTATIONS = {
                              "shift = np.where(visible, Aj - Afin[:, None], 0.0)"),
     "running_no_clip": ("ex = np.minimum(ex, L - 1)", "ex = ex"),
     "running_flush_threshold": ("keep = visible & (ex <= L - 1)", "keep = visible & (ex <= L)"),
+    "minmax_flush_applied": ("whose window can end above the row minimum.\n    flush = flush and window is not None",
+                             "whose window can end above the row minimum.\n    flush = flush"),
     "trunc_takes_unit_weights": ("w = np.where(kept, np.exp(np.where(kept, S - m[:, None], 0.0)), 0.0)\n        else:",
                                  "w = kept.astype(np.float64)\n        else:"),
 }

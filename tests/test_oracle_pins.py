@@ -51,6 +51,8 @@ VARIANTS = [
     dict(kind="kint", levels=4, window=3.0, flush=True),
     dict(kind="kint", levels=16, window=8.0, interp=True),
     dict(kind="kint", levels=4, window=3.0, interp=True, flush=True),
+    dict(kind="kint", levels=4, flush=True),
+    dict(kind="kint", levels=7, interp=True, flush=True),
 ]
 
 

@@ -95,3 +95,21 @@ def test_level_count_and_kind_checks():
         oracle.head_bwd(np.ones((2, 2)), np.ones((2, 2)), np.ones((2, 2)), np.ones((2, 2)), kind="pot_running",
                         levels=4)
     assert oracle.qsa_oracle.ANCHOR_TILE == 64
+
+
+def test_anchor_override():
+    # the anchors an implementation in lower precision may produce enter as an input: the
+    # definition's own sequence reproduces the default, and raising every anchor by one moves
+    # every exponent up one level (weights halved where the clip does not bind)
+    q, k, v = _qkv(150, d=8, sigma=1.0, seed=31)
+    base = oracle.head_rows(q, k, v, kind="pot_running", levels=64, detail=True)
+    S = (q @ k.T) / math.sqrt(8)
+    nt = 3
+    tmax = np.stack([(S[:, c * 64:(c + 1) * 64] / math.log(2.0)).max(1) for c in range(nt)], 1)
+    A = np.ceil(np.maximum.accumulate(tmax, 1))
+    same = oracle.head_rows(q, k, v, kind="pot_running", levels=64, detail=True, anchors=A)
+    np.testing.assert_array_equal(same["w"], base["w"])
+    up = oracle.head_rows(q, k, v, kind="pot_running", levels=64, detail=True, anchors=A + 1)
+    np.testing.assert_array_equal(up["idx"].astype(int), base["idx"].astype(int) + 1)
+    np.testing.assert_array_equal(up["w"], base["w"] / 2)
+    np.testing.assert_array_equal(up["O"], base["O"])

@@ -16,8 +16,10 @@ from tests import parity
 F = np.float32
 
 
-def emulate(var, q, k, v, causal):
-    """fp32 emulation of one head: scores in float32 (BLAS order), weights via fp32 ops."""
+def emulate(var, q, k, v, causal, anchor_override=()):
+    """fp32 emulation of one head: scores in float32 (BLAS order), weights via fp32 ops.
+    anchor_override (pot_running): (row, tile, value) entries that replace the rounded-up
+    maximum of that tile before the running maximum is taken."""
     q32, k32, v32 = q.astype(F), k.astype(F), v.astype(F)
     N, d = q.shape
     sc = F(1.0 / math.sqrt(d))
@@ -38,8 +40,11 @@ def emulate(var, q, k, v, causal):
         c = F(sc * F(1.4426950408889634))
         raw = np.where(vis, acc, -np.inf).astype(F)
         nt = (N + 63) // 64
-        cm = np.maximum.accumulate(np.stack([raw[:, j * 64:(j + 1) * 64].max(1) for j in range(nt)], 1), 1)
-        A = np.ceil((cm * c).astype(F)).astype(np.float64)
+        tm = np.stack([raw[:, j * 64:(j + 1) * 64].max(1) for j in range(nt)], 1)
+        a = np.ceil((tm * c).astype(F)).astype(np.float64)
+        for (i, j, val) in anchor_override:
+            a[i, j] = val
+        A = np.maximum.accumulate(a, 1)
         Aj = np.repeat(A, 64, axis=1)[:, :N]
         e = np.rint(Aj - acc.astype(np.float64) * np.float64(c))
         shift = A[:, -1:] - Aj
@@ -138,3 +143,36 @@ def test_wrong_index_outside_band_fails():
     O2[3] *= 1.05
     with pytest.raises(AssertionError):
         parity.compare_head(var, q, k, v, np.arange(N), O2, idx, causal=False, tol=1e-2)
+
+
+def _on_integer_anchor(N=150, d=64, row=100, key=10, n=3, seed=8):
+    """Inputs whose row `row` has its largest score of key tile 0 at key `key`, equal to
+    n ln 2 up to float64 rounding: that tile's anchor is n or n + 1 in fp32."""
+    r = np.random.default_rng(seed)
+    q, k, v = r.standard_normal((N, d)) * 0.5, r.standard_normal((N, d)) * 0.5, r.standard_normal((N, d))
+    sc = 1.0 / math.sqrt(d)
+    k[key] = q[row] * (n * math.log(2.0) / (sc * (q[row] @ q[row])))
+    return q, k, v
+
+
+def test_single_pass_ambiguous_anchor_either_way_passes():
+    q, k, v = _on_integer_anchor()
+    var = dict(kind="pot_running", levels=8)
+    cands = parity.anchor_candidates(var, q, k, np.arange(150), causal=False)
+    assert len(cands[100]) == 2 and {c[0] for c in cands[100]} == {3.0, 4.0}
+    for val in (3.0, 4.0):   # the emulation takes either rounding of the tile maximum
+        O, idx = emulate(var, q, k, v, False, anchor_override=[(100, 0, val)])
+        rep, _ = parity.compare_head(var, q, k, v, np.arange(150), O, idx, causal=False, tol=1e-4)
+        assert rep.idx_bad == 0 and rep.anchor_amb_rows >= 1
+
+
+def test_single_pass_wrong_anchor_fails():
+    q, k, v = _on_integer_anchor()
+    var = dict(kind="pot_running", levels=8)
+    O, idx = emulate(var, q, k, v, False)
+    A0 = np.ceil(np.max(q[7] @ k[:64].T) / 8.0 / math.log(2.0))
+    cands = parity.anchor_candidates(var, q, k, np.arange(150), causal=False)
+    assert len(cands[7]) == 1                    # row 7's anchors are decided
+    O2, idx2 = emulate(var, q, k, v, False, anchor_override=[(7, 0, A0 + 1)])
+    with pytest.raises(AssertionError):
+        parity.compare_head(var, q, k, v, np.arange(150), O2, idx2, causal=False, tol=1e-4)
