@@ -4,32 +4,40 @@
 // -> Row max (anchor point) -> Power-of-two weights -> PV matmul -> Output"),
 // laid out for CDNA4:
 //
-//   * one workgroup = 4 waves = 128 query rows of one (batch, head); each
-//     wave owns 32 rows for the whole kernel (its Q^T operand stays in VGPRs);
+//   * one workgroup = 4 waves = 128 query rows of one (batch, head), two
+//     workgroups per CU (two waves per SIMD); each wave owns 32 rows for the
+//     whole kernel (its Q^T operand stays in VGPRs);
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: lane (i, h) of a wave holds query row i and 16
-//     keys of each 32-key block, so row maxima, minima and sums are in-lane
-//     reductions plus one exchange between the two half-waves;
+//     keys of each 32-key block, so row maxima are in-lane reductions plus one
+//     exchange between the two half-waves;
 //   * the accumulator layout of S^T is the B operand of O^T = V^T P^T, so P
-//     never moves between lanes;
-//   * anchored kinds run a pre-pass over all key tiles for the true row
-//     maximum (and minimum for min-max calibration).  The main loop then
-//     starts each score accumulation at -M (a register vector holding the
-//     row max), so the MFMA itself delivers s' = acc - M <= 0 and the weight
-//     needs no per-element subtraction; O needs no per-tile rescale;
-//   * the online exact control skips the pre-pass and rescales O by
+//     never moves between lanes; the row sums of P are one more MMA per P
+//     operand against a constant 0/1 selector (v_dot2_f32_bf16 stalls the
+//     matrix core of its SIMD for several times its issue cost);
+//   * anchored kinds get the true row extrema from rowext_bf16, a kernel of
+//     its own launched first (64 rows per wave, so each K operand read feeds
+//     two MMAs), which parks them in O; the main loop starts each score
+//     accumulation at -M, so the MFMA itself delivers s' = acc - M;
+//   * the online exact control has no pre-pass and rescales O by
 //     2^(m_old - m_new) when a row's running maximum grows;
-//   * K and V tiles of 64 keys are double-buffered in LDS and filled by
-//     buffer loads that write LDS directly (no staging registers; hardware
-//     zero-fill past the end of the head), one tile ahead, with one workgroup
-//     barrier per tile.  K rows are padded to an odd number of 16-byte slots
-//     so a column read by 16 lanes hits 16 different banks; V stays row-major
-//     and the V^T operand comes from transposing LDS reads (ds_read_b64_tr_b16);
-//   * the scores of tile t+1 are computed on the matrix cores while the
-//     weights of tile t are formed on the VALU, so the two overlap in a wave;
-//   * only a wave's last tile can need masking (causal diagonal or the ragged
-//     end of the sequence); it runs a separate code path, so the steady-state
-//     tiles carry no mask arithmetic.
+//   * software pipeline, three tiles deep: iteration t multiplies P(t) (formed
+//     in iteration t-1) by the V tile t, forms the weights of tile t+1 (whose
+//     scores were issued in iteration t-1) and issues the scores of tile t+2,
+//     so the PV MMAs and the score MMAs never wait for this iteration's VALU
+//     work and the weights never wait for this iteration's MMAs;
+//   * K and V tiles of 64 keys sit in two LDS stages each, unpadded, with the
+//     16-byte chunks of each row XOR-swizzled so that the score operand reads
+//     (ds_read_b128) and the transposing V reads (ds_read_b64_tr_b16) are free
+//     of bank conflicts.  They are filled by buffer loads that write LDS
+//     directly (no staging registers; hardware zero-fill past the end of the
+//     head), the same number of instructions in every wave, issued right after
+//     the iteration's V operand reads (the compiler makes transposing LDS reads
+//     wait for every LDS-direct load issued before them);
+//   * K-interval grid values come from a per-row table of T_l in LDS (K+1
+//     values per row, no transcendental per element; interpolation takes
+//     T_l+1 = T_l e^-Delta) for K <= 16; larger K evaluates T_l = 2^(l step)
+//     per element.
 #include "qsa_common.h"
 #include "qsa_mfma_util.h"
 #include "qsa_weights.h"
@@ -37,38 +45,61 @@
 namespace qsa {
 namespace {
 
-constexpr int NW = 4;    // waves per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int SH = 9;    // log2(BM * 4): the row-constant template's table stride (no table is built here)
-#ifndef QSA_BF16_WAVES_PER_SIMD
-#define QSA_BF16_WAVES_PER_SIMD 2
-#endif
+constexpr int NW = 4;   // waves per workgroup
+constexpr int BN = 64;  // keys per tile
+constexpr int NS = 2;   // K and V stages in LDS
+constexpr int KTAB_MAX = 16;  // largest K with a per-row grid table in LDS
+constexpr int BM = NW * 32;   // query rows per workgroup
+constexpr int SH = 9;         // log2(BM * 4): the K-interval table's stride between grid values of one row
 
-template <int D, int WK, bool DUMP>
-__global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(FwdArgs a) {
+// Slot of 16-byte chunk q of K row r is q ^ kswz(r): a ds_read_b128 of the score loop reads
+// one chunk of 32 consecutive rows, and the XOR spreads every 16-lane group (and every 8-lane
+// group) over distinct bank groups.
+template <int D>
+__device__ __forceinline__ int kswz_of(int r) {
+  return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+// Slot of 16-byte chunk q of V row r is q ^ vswz(r): a transposing read touches rows 4h + 0..3
+// (plus multiples of 8), two chunks per row, and the XOR on the row's low bits puts those rows'
+// chunks on distinct bank groups for 8-, 16- and 32-lane groups alike.
+template <int D>
+__device__ __forceinline__ int vswz_of(int r) {
+  return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+}
+
+// Byte layout: NS K stages, then NS V stages (rows of D bf16, no padding), then the table.
+template <int D> struct Lay {
+  static constexpr int SL = D / 8;             // 16-byte slots per row
+  static constexpr int RR = SL * 16;           // bytes per row
+  static constexpr int KT = BN * RR, VT = BN * RR;
+  static constexpr int V0 = NS * KT;           // first V stage
+  static constexpr int TAB = NS * (KT + VT);   // K-interval table
+  static constexpr int LW = SL / NW;           // tile-load instructions per wave (64 slots each)
+  static_assert(SL % NW == 0, "tiles split evenly over the waves");
+};
+
+template <int D, int WK, bool DUMP, bool TAB>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
-  constexpr int C8 = D / 8;   // 16-byte chunks per K row
-  constexpr int SK = D / 8 + 1;    // 16-byte slots per K row in LDS (odd: 16 rows -> 16 bank groups)
-  constexpr int SV = D / 8 + 4;    // slots per V row (row stride = 64 mod 256 bytes)
-  constexpr int KR = SK * 16, VR = SV * 16;
-  constexpr int KT = BN * KR, VT = BN * VR;  // bytes of one K / V tile buffer
-  constexpr int KIW = (SK + NW - 1) / NW;    // direct-load instructions per wave per K tile (max)
-  constexpr int VIW = (SV + NW - 1) / NW;
+  using LY = Lay<D>;
+  constexpr int SL = LY::SL, RR = LY::RR, KT = LY::KT, VT = LY::VT, LW = LY::LW;
   constexpr bool RUN = wk_running(WK);             // single-pass PoT: running integer anchor
-  constexpr bool ANCH = (WK != WK_EXACT) && !RUN;  // true-row-extrema pre-pass
+  constexpr bool ANCH = (WK != WK_EXACT) && !RUN;  // row extrema from the pre-pass
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
   constexpr bool POT = wk_pot(WK);
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
+  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH);
   constexpr bool SUPPORT = wk_support(WK), UNIF = (WK == WK_UNIF);
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_POTR_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
 
   extern __shared__ __align__(16) unsigned char smem[];
   lds_u8* const lds = (lds_u8*)smem;
+  unsigned char* const Tb = smem + LY::TAB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
   int bh, qt;
   map_block(a, bh, qt);
@@ -78,12 +109,13 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   const int q0 = qt * BM;
   const int wr0 = q0 + wave * 32;
   const int row = wr0 + li;
+  const int lim = a.causal ? min(row, N - 1) : N - 1;  // last key visible to this lane's row
   const __bf16* Qg = (const __bf16*)a.q + (size_t)(b * a.H + h) * N * D;
   const size_t kv_off = (size_t)(b * a.Hkv + kvh) * N * D;
   const __bf16* const Kg = (const __bf16*)a.k + kv_off;
   const __bf16* const Vg = (const __bf16*)a.v + kv_off;
 
-  // Q^T operand: lane (li, hh) holds Q[row][16c + 8hh .. +7].
+  // Q^T operand: lane (li, hh) holds Q[row][16c + 8hh .. +7] (rows past N: 0)
   u32x4 qf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c)
@@ -93,316 +125,173 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
   // last tile this wave computes (-1: none); only that tile can need masking
   const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
   const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
+  const int tclean = last_masked ? wlast : wlast + 1;  // tiles t < tclean need no mask
 
-  // ---- tile staging: buffer loads straight into LDS ------------------------
-  // A wave-instruction writes 64 consecutive 16-byte slots; slot s of a tile
-  // is row s / SK, chunk s % SK of the padded layout (pad chunks load zeros
-  // from an out-of-range offset).  The per-tile buffer resource starts at the
-  // tile and ends at the end of the head, so rows past N read as zero.
-  uint32_t kvo[KIW], vvo[VIW];
-#pragma unroll
-  for (int m = 0; m < KIW; ++m) {
-    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK, c = sl % SK;
-    kvo[m] = c < D / 8 ? (uint32_t)(j * D + c * 8) * 2 : 0x7FFFFFF0u;
+  // ---- tile staging: buffer loads straight into LDS ------------------------------------------
+  // Instruction m of a wave writes the 64 consecutive 16-byte slots (wave + NW m) * 64 + lane:
+  // slot s of a tile is row j = s / SL, position s % SL of the row, which holds chunk
+  // (s % SL) ^ swz(j).  The per-tile buffer resource starts at the tile and ends at the end of
+  // the head, so rows past N read as zero.
+  // Instruction m covers rows 64 NW m / SL further on than instruction 0 (a multiple of 16), the
+  // same position in the row and the same swizzle (which reads row bits below 4): its global
+  // offset is instruction 0's plus m * 64 NW * 16 bytes, taken as the scalar offset.
+  uint32_t kvo, vvo;
+  {
+    const int sl = wave * 64 + lane, j = sl / SL, c = sl % SL;
+    kvo = (uint32_t)(j * D + 8 * (c ^ kswz_of<D>(j))) * 2;
+    vvo = (uint32_t)(j * D + 8 * (c ^ vswz_of<D>(j))) * 2;
   }
-#pragma unroll
-  for (int m = 0; m < VIW; ++m) {
-    const int sl = (wave + NW * m) * 64 + lane, j = sl / SV, c = sl % SV;
-    vvo[m] = c < D / 8 ? (uint32_t)(j * D + c * 8) * 2 : 0x7FFFFFF0u;
-  }
+  static_assert((NW * 64 / SL) % 16 == 0, "the swizzles repeat every 16 rows");
   auto tile_rsrc = [&](const __bf16* base, int kt) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D * 2,
                                              0x00020000);
   };
-  auto load_k = [&](int kt, int buf) {
+  auto load_k = [&](int kt, int st) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kg, kt);
 #pragma unroll
-    for (int m = 0; m < KIW; ++m)
-      if (wave + NW * m < SK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + NW * m) * 1024), 16,
-                                                 kvo[m], 0, 0, 0);
+    for (int m = 0; m < LW; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + st * KT + (wave + NW * m) * 1024), 16, kvo,
+          m * NW * 64 * 16, 0, 0);
   };
-  auto load_v = [&](int kt, int buf) {
+  auto load_v = [&](int kt, int st) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
 #pragma unroll
-    for (int m = 0; m < VIW; ++m)
-      if (wave + NW * m < SV)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + 2 * KT + buf * VT + (wave + NW * m) * 1024), 16, vvo[m], 0, 0, 0);
+    for (int m = 0; m < LW; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + LY::V0 + st * VT + (wave + NW * m) * 1024), 16, vvo,
+          m * NW * 64 * 16, 0, 0);
   };
-  // this wave's LDS-direct loads have landed (before the workgroup barrier)
   auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // A-operand read offsets (the tile buffer and the 32-key block are added as constants)
-  const uint32_t koff = li * KR + hh * 16;  // + 32 c for k-step c
-  // V^T operand: in each 16-lane group, lane 4q + p points at V[key q][4p .. 4p+3] of the
-  // group's 16 columns; the transposing read hands lane l column l and keys q = 0..3.
-  const uint32_t vtr = (4 * hh + ((lane & 15) >> 2)) * VR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-  // 32-key block kb of a tile: init + K_block Q^T  (init: the -M vector, or 0)
-  auto qk1 = [&](int buf, int kb, const f32x16& init) {
-    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR + koff;
+  // QK A-operand for k-step c: lane (li, hh) reads chunk 2c + hh of K row li (keys of the block)
+  uint32_t koff[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = li * RR + 16 * ((2 * c + hh) ^ kswz_of<D>(li));
+  // V^T operand: in each 16-lane group g, lane 4q + p points at V[key 4hh + q][4p .. 4p+3] of the
+  // group's 16 columns (column block db, half g & 1): chunk 4db + 2(g & 1) + p/2 of the row,
+  // at its swizzled slot; the transposing read hands lane l column l and keys q = 0..3.  The
+  // row offsets 16(2kb + kc) and 8 keep the row's low bits, so the swizzle is per lane.
+  const int vq = (lane & 15) >> 2, vg1 = (lane >> 4) & 1, vp = lane & 3;
+  uint32_t vtr[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    vtr[db] = (4 * hh + vq) * RR + 16 * ((4 * db + 2 * vg1 + (vp >> 1)) ^ vswz_of<D>(vq)) + 8 * (vp & 1);
+
+  // 32-key block kb of the K tile in stage st: init + K_block Q^T  (init: the -M vector, or 0)
+  auto qk1 = [&](int st, int kb, const f32x16& init) __attribute__((always_inline)) {
+    const lds_u8* kbase = lds + st * KT + kb * 32 * RR;
     f32x16 s = init;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *(const __attribute__((address_space(3))) u32x4*)(kbase + 32 * c);
-      s = mma(ka, qf[c], c == 0 ? init : s);
-    }
+    for (int c = 0; c < KC; ++c) s = mma(*(const lds_u32x4*)(kbase + koff[c]), qf[c], c == 0 ? init : s);
     return s;
   };
-  auto qk = [&](int buf, f32x16 (&s)[2], const f32x16& init) {
-    s[0] = qk1(buf, 0, init);
-    s[1] = qk1(buf, 1, init);
-  };
-  // O^T += V^T P^T over the 32 keys of block kb (k-steps g = 2kb, 2kb+1)
-  auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
-    const lds_u8* vbase = lds + 2 * KT + buf * VT + vtr;
+
+  // Row sums on the matrix core: v_mfma_f32_16x16x32_bf16 with A a constant 0/1 selector and B
+  // a P^T operand as it is.  In the 16x16x32 layout lane l holds B rows (keys) 8(l/16)..+7 of
+  // column l % 16; in the P^T operand the same lane holds 8 keys of query row l % 32.  The
+  // selector's rows 0-7 take the k-groups 0 and 2 (query n = l % 16, both key halves) and rows
+  // 8-15 the k-groups 1 and 3 (query n + 16), so C[m][n] accumulates the row sum of query n
+  // (m < 8) or n + 16 (m >= 8): lane l holds the sum of query q(l) = l, l - 16, l - 16, l - 32
+  // for its four 16-lane groups.
+  const uint32_t rsel = (((lane & 15) < 8) == (((lane >> 4) & 1) == 0)) ? 0x3F803F80u : 0u;  // bf16 1.0 pairs
+  const u32x4 rs_sel = {rsel, rsel, rsel, rsel};
+  const int rs_q = lane < 16 ? lane : (lane < 48 ? lane - 16 : lane - 32);
+
+  f32x16 o[DB];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * VR + 64 * db;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * VR));
-        const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-        o[db] = mma(va, P[kc], o[db]);
-      }
-  };
-  // keys up to `lim` are visible to this lane's row
-  const int lim = a.causal ? min(row, N - 1) : N - 1;
-  auto mask_fill = [&](f32x16 (&s)[2], int kt, float fill) {
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  f32x4 rs = {0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4 P[2][2];  // weights of the tile PV multiplies next: [kb][kc]
+  // O^T += V^T P^T over the V tile in stage st (two transposing reads per operand), and the row sums
+  auto pv = [&](int st) __attribute__((always_inline)) {
+    const lds_u8* vbase = lds + LY::V0 + st * VT;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = (kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : fill;
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * RR + vtr[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * RR));
+          const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+          o[db] = mma(va, P[kb][kc], o[db]);
+        }
+        rs = mma16(rs_sel, P[kb][kc], rs);
+      }
   };
 
-  // ---- pre-pass: true row extrema ------------------------------------------
+  // ---- row extrema of the anchored kinds ----------------------------------------------------
+  // rowext_bf16 parked them as raw accumulator values, 8 bytes per row packed at the start of
+  // the wave's own 32 rows of O (a contiguous 256-byte run), which this wave later overwrites
   float M = -__builtin_inff(), MN = __builtin_inff();
-  const f32x16 zero16 = {};
   if (ANCH) {
-    const bool tmin = a.track_min;
-    load_k(0, 0);
-    if (T > 1) load_k(1, 1);
-    loads_done();
-    __syncthreads();
-    f32x16 s[2];
-    if (wlast >= 0) qk(0, s, zero16);
-    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-    // tiles before the wave's last (no masking), then the last tile and the iterations in
-    // which the wave only issues its share of the other waves' loads: two loops, so that the
-    // masking code stays out of the first (every wave still passes T barriers)
-    // (unrolled by two with the score registers swapping roles, as in the main loop)
-    auto fold = [&](const f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) __attribute__((always_inline)) {
-      if (t + 2 < T) load_k(t + 2, t & 1);  // buffer t&1 was last read in iteration t-1
-      qk((t + 1) & 1, nxt, zero16);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) M = fmaxf(M, cur[kb][r]);
-      if (tmin) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) MN = fminf(MN, cur[kb][r]);
-      }
-      loads_done();
-      __syncthreads();
-    };
-    f32x16 s2[2];
-    int t = 0;
-    for (; t + 1 < wlast; t += 2) {
-      fold(s, s2, t);
-      fold(s2, s, t + 1);
-    }
-    if (t < wlast) {
-      fold(s, s2, t);
-      s[0] = s2[0];
-      s[1] = s2[1];
-      ++t;
-    }
-    for (; t < T; ++t) {
-      if (t + 2 < T) load_k(t + 2, t & 1);
-      if (t == wlast) {
-        f32x16 sm[2] = {s[0], s[1]};
-        if (last_masked) mask_fill(sm, t, -__builtin_inff());
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) M = fmaxf(M, sm[kb][r]);
-        if (tmin) {
-          if (last_masked) mask_fill(s, t, __builtin_inff());
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) MN = fminf(MN, s[kb][r]);
-        }
-      }
-      loads_done();
-      __syncthreads();
-    }
-    M = half_max(M);
-    MN = half_min(MN);
+    const uint32_t* const park = (const uint32_t*)((const __bf16*)a.o + ((size_t)bh * N + wr0) * D) + 2 * li;
+    M = row < N ? bitsf(park[0]) : 0.0f;
+    MN = row < N ? bitsf(park[1]) : 0.0f;
   }
-
-  RowC rc = make_row<WK, SH>(a, M, MN, wave * 32 + li, nullptr, hh, 2);
+  RowC rc = make_row<WK, SH, true>(a, M, MN, wave * 32 + li, TAB ? Tb : nullptr, hh, 2);
+  // interpolation: T_l+1 = T_l e^-Delta = T_l 2^step
+  const float rstep = INTERP && TAB ? __builtin_amdgcn_exp2f(rc.step) - 1.0f : 0.0f;
   // main-loop score accumulators start at -M: s' = acc - M
-  f32x16 init16;
+  f32x16 init;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
+  for (int r = 0; r < 16; ++r) init[r] = ANCH ? -M : 0.0f;
+
   // PoT rounds t = G - y to an integer in one FMA, G = 2^24 (pre-pass kinds: scores start at
   // -M, so t = 2^24 + acc' c) or G = 1.5 * 2^23 (single pass: t = (G - A) + acc c, and G - A
   // must be exact in fp32 for a negative integer anchor A too, which 2^24 - A is not).  In
   // both cases t lies in [2^23, 2^24), bits(t) = bits(G) - e, and the low 16 bits are -e.
   constexpr int32_t pot_bits = RUN ? 0x4B400000 : 0x4B800000;  // bits of G
   constexpr float pot_g = RUN ? 12582912.0f : 16777216.0f;      // G
-  int32_t pot_lo = pot_bits - (a.levels - 1);                   // bits of G - (L-1): the clip e <= L-1
+  const int L = a.levels;
+  const float Kf = (float)a.levels;
+  int32_t pot_lo = pot_bits - (L - 1);  // bits of G - (L-1): the clip e <= L-1
   // Single-pass PoT: A = ceil(running max of s log2 e), an integer.  The weights are formed
   // against a lagging integer anchor Aw <= A (tb = G - Aw) with the clip moved by the lag
   // dl = A - Aw (pot_lo = bits(G) - (L-1) + dl), so every weight carries the same factor 2^dl
-  // relative to A while Aw stays; O and l are rescaled only when Aw moves, on the first tile
-  // and when the lag would pass 32 (bf16 weights up to 2^32 and their sums stay well inside
-  // the exponent range).
+  // relative to A while Aw stays; O and the row sums are rescaled only when Aw moves, on the
+  // first tile and when the lag would pass 32 (bf16 weights up to 2^32 and their sums stay well
+  // inside the exponent range).
   float A = -__builtin_inff(), Aw = -__builtin_inff();
   int dlag = 0;
   float tb = pot_g;
-  const int L = a.levels;
-  const float Kf = (float)a.levels;
 
-  // weights of 32-key block kb of tile kt -> 2 P^T operands (bf16) and the row sum
-  auto weights = [&](const f32x16& sb, int kb, u32x4 (&P)[2], float& l, int kt, bool masked) {
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int r0 = 8 * kc + 2 * p;
-          const float x0 = sb[r0], x1 = sb[r0 + 1];
-          uint32_t pk;
-          uint32_t i0 = 0, i1 = 0;  // grid indices (dump only)
-          if (EXACT_W) {
-            // exact: 2^((acc - M) c); the online kind folds -M c into the FMA
-            const float y0 = ANCH ? x0 * rc.c : fmaf(x0, rc.c, -rc.mc);
-            const float y1 = ANCH ? x1 * rc.c : fmaf(x1, rc.c, -rc.mc);
-            pk = pack_bf16(__builtin_amdgcn_exp2f(y0), __builtin_amdgcn_exp2f(y1));
-          } else if (SUPPORT) {
-            // truncation / uniform weighting: keys with y = (M - acc) c > W log2 e are outside
-            // the support; inside, exp(s - m) or 1
-            const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
-            const float e0 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x0 * rc.c);
-            const float e1 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x1 * rc.c);
-            pk = pack_bf16(y0 > rc.cut ? 0.0f : e0, y1 > rc.cut ? 0.0f : e1);
-            if (DUMP) {
-              i0 = y0 > rc.cut ? 254u : 0u;
-              i1 = y1 > rc.cut ? 254u : 0u;
-            }
-          } else if (POT && !FLUSH) {
-            // t = 2^24 + (acc - M) c = 2^24 - y, rounded to an integer by the FMA itself
-            const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
-            pk = pot_pair(t0, t1, pot_lo);
-            if (DUMP) {
-              i0 = 127u - ((pk >> 7) & 0x1FFu) + (uint32_t)dlag;  // against the running anchor
-              i1 = 127u - ((pk >> 23) & 0x1FFu) + (uint32_t)dlag;
-            }
-          } else if (POT) {  // flush: e >= L -> 0
-            const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
-            const int32_t lo = pot_lo;
-            const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
-            const uint32_t w0 = b0 < lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
-            const uint32_t w1 = b1 < lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
-            pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-            if (DUMP) {
-              i0 = b0 < lo ? 254u : (uint32_t)(pot_bits - b0 + dlag);
-              i1 = b1 < lo ? 254u : (uint32_t)(pot_bits - b1 + dlag);
-            }
-          } else if (KHARD) {
-            // y = (M - acc) c; t = y + 2^23 rounds y: bits(t) = 0x4B000000 + l
-            const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
-            int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
-            b0 = min(max(b0, 0x4B000000), 0x4B000000 + L);
-            b1 = min(max(b1, 0x4B000000), 0x4B000000 + L);
-            float w0 = __builtin_amdgcn_exp2f(rc.step * (float)(b0 - 0x4B000000));  // T_l
-            float w1 = __builtin_amdgcn_exp2f(rc.step * (float)(b1 - 0x4B000000));
-            const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;
-            if (FLUSH) {  // y > K: below the window
-              w0 = y0 > Kf ? 0.0f : w0;
-              w1 = y1 > Kf ? 0.0f : w1;
-            }
-            pk = pack_bf16(w0, w1);
-            if (DUMP) {
-              i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
-              i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
-            }
-          } else {  // K-interval, interpolation
-            const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
-            const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
-            const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
-            const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
-            typedef float f2 __attribute__((ext_vector_type(2)));
-            const f2 e0 = kgrid_pair(rc.step, f0);  // (T_l, T_l+1 - T_l)
-            const f2 e1 = kgrid_pair(rc.step, f1);
-            float w0 = fmaf(c0 - f0, e0.y, e0.x), w1 = fmaf(c1 - f1, e1.y, e1.x);
-            if (FLUSH) {
-              w0 = y0 > Kf ? 0.0f : w0;
-              w1 = y1 > Kf ? 0.0f : w1;
-            }
-            pk = pack_bf16(w0, w1);
-            if (DUMP) {
-              i0 = (FLUSH && y0 > Kf) ? 254u : l0;
-              i1 = (FLUSH && y1 > Kf) ? 254u : l1;
-            }
-          }
-          if (masked) {
-            const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);  // r0 even: keys k0, k0 + 1
-            const uint32_t m0 = k0 <= lim ? 0x0000FFFFu : 0u, m1 = k0 + 1 <= lim ? 0xFFFF0000u : 0u;
-            pk &= (m0 | m1);
-            if (DUMP) {
-              i0 = k0 <= lim ? i0 : 255u;
-              i1 = k0 + 1 <= lim ? i1 : 255u;
-            }
-          }
-          if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
-            const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);
-            uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
-            if (k0 < N) dst[k0] = (uint8_t)i0;
-            if (k0 + 1 < N) dst[k0 + 1] = (uint8_t)i1;
-          }
-          P[kc][p] = pk;
-          l = dot2_ones(pk, l);
-        }
-  };
-
-  // online exact: grow the running max over this tile, rescale O and l
-  auto online_max = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l) {
-    float tm = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[kb][r]);
-    const float mnew = fmaxf(M, half_max(tm));
-    if (__builtin_amdgcn_ballot_w64(mnew > M)) {
-      const float alpha = mnew > M ? __builtin_amdgcn_exp2f((M - mnew) * rc.c) : 1.0f;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      M = mnew;
-      rc.mc = mnew * rc.c;
-    }
-  };
-
-  // single-pass PoT: fold this tile's maximum into the anchor before its weights are formed;
-  // when the weight anchor Aw has to move, O and l, formed against the old Aw, are scaled by
-  // 2^(Aw_old - Aw) (exact)
-  auto run_anchor = [&](const f32x16 (&s)[2], f32x16 (&o)[DB], float& l, int kt, bool masked) {
+  // scale the row sums by each row's factor (held by the lane of that row)
+  auto rs_scale = [&](float alpha) { rs *= bitsf(__builtin_amdgcn_ds_bpermute(4 * rs_q, (int)fbits(alpha))); };
+  // the tile's maximum of this lane's row (masked: visible keys only), both half-waves combined
+  auto tile_max = [&](const f32x16 (&s)[2], bool masked, int kt) __attribute__((always_inline)) {
     float tm = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         tm = fmaxf(tm, (!masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim) ? s[kb][r] : -__builtin_inff());
-    const float An = fmaxf(A, __builtin_ceilf(half_max(tm) * rc.c));
+    return half_max(tm);
+  };
+  // online exact: grow the running max over a tile, rescale O and the row sums
+  auto online_max = [&](const f32x16 (&s)[2], bool masked, int kt) __attribute__((always_inline)) {
+    const float mnew = fmaxf(M, tile_max(s, masked, kt));
+    if (__builtin_amdgcn_ballot_w64(mnew > M)) {
+      const float alpha = mnew > M ? __builtin_amdgcn_exp2f((M - mnew) * rc.c) : 1.0f;
+      rs_scale(alpha);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      M = mnew;
+      rc.mc = mnew * rc.c;
+    }
+  };
+  // single-pass PoT: fold a tile's maximum into the anchor before its weights are formed; when
+  // the weight anchor Aw has to move, O and the row sums, formed against the old Aw, are scaled
+  // by 2^(Aw_old - Aw) (exact)
+  auto run_anchor = [&](const f32x16 (&s)[2], bool masked, int kt) __attribute__((always_inline)) {
+    const float An = fmaxf(A, __builtin_ceilf(tile_max(s, masked, kt) * rc.c));
     if (__builtin_amdgcn_ballot_w64(An - Aw > 32.0f)) {  // Aw = -inf before the first tile
       const bool move = An - Aw > 32.0f;
       const float alpha = move ? (Aw > -__builtin_inff() ? __builtin_ldexpf(1.0f, (int)(Aw - An)) : 0.0f) : 1.0f;
-      l *= alpha;
+      rs_scale(alpha);
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       Aw = move ? An : Aw;
@@ -410,79 +299,211 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
     }
     A = An;
     dlag = (int)(A - Aw);
-    pot_lo = pot_bits - (a.levels - 1) + dlag;
+    pot_lo = pot_bits - (L - 1) + dlag;
   };
 
-  // ---- main loop --------------------------------------------------------------
-  f32x16 o[DB];
+  // weights of 32-key block kb of tile kt -> the two P^T operands P[kb] (bf16)
+  auto weights = [&](const f32x16& sb, int kb, int kt, bool masked) __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float l = 0.0f;
-  __syncthreads();  // pre-pass reads done before the buffers are refilled
-  load_k(0, 0);
-  load_v(0, 0);
-  if (T > 1) load_k(1, 1);
-  loads_done();
-  __syncthreads();
-  f32x16 s[2];
-  if (wlast >= 0) qk(0, s, init16);
-  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
-  // Tiles before the wave's last (unmasked), then its last tile and the iterations in which it
-  // only issues its share of the other waves' loads: two loops, so that the masking code stays
-  // out of the first (merged into one body it ran on every tile); every wave passes T barriers.
-  // the scores of tile t+1 go to the other of two register sets, whose roles swap every
-  // iteration (unrolled by two), so no copy of 32 registers per tile
-  auto steady = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int t) __attribute__((always_inline)) {
-    if (t + 2 < T) load_k(t + 2, t & 1);      // buffers last read in iteration t-1
-    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
-    // block 0 of tile t+1 on the matrix cores while block 0 of tile t is weighted
-    nxt[0] = qk1((t + 1) & 1, 0, init16);
-    if (WK == WK_EXACT) online_max(cur, o, l);
-    if (RUN) run_anchor(cur, o, l, t, false);
-    u32x4 P[2];
-    weights(cur[0], 0, P, l, t, false);
-    pv1(t & 1, 0, P, o);
-    nxt[1] = qk1((t + 1) & 1, 1, init16);
-    weights(cur[1], 1, P, l, t, false);
-    pv1(t & 1, 1, P, o);
-    loads_done();
-    __syncthreads();
-  };
-  f32x16 s2[2];
-  int t = 0;
-  for (; t + 1 < wlast; t += 2) {
-    steady(s, s2, t);
-    steady(s2, s, t + 1);
-  }
-  if (t < wlast) {
-    steady(s, s2, t);
-    s[0] = s2[0];
-    s[1] = s2[1];
-    ++t;
-  }
-  for (; t < T; ++t) {
-    if (t + 2 < T) load_k(t + 2, t & 1);
-    if (t + 1 < T) load_v(t + 1, (t + 1) & 1);
-    if (t == wlast) {
-      if (WK == WK_EXACT) {
-        f32x16 sm[2] = {s[0], s[1]};
-        if (last_masked) mask_fill(sm, t, -__builtin_inff());
-        online_max(sm, o, l);
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r0 = 8 * kc + 2 * p;
+        const float x0 = sb[r0], x1 = sb[r0 + 1];
+        uint32_t pk;
+        uint32_t i0 = 0, i1 = 0;  // grid indices (dump only)
+        if (EXACT_W) {
+          // exact: 2^((acc - M) c); the online kind folds -M c into the FMA
+          const float y0 = ANCH ? x0 * rc.c : fmaf(x0, rc.c, -rc.mc);
+          const float y1 = ANCH ? x1 * rc.c : fmaf(x1, rc.c, -rc.mc);
+          pk = pack_bf16(__builtin_amdgcn_exp2f(y0), __builtin_amdgcn_exp2f(y1));
+        } else if (SUPPORT) {
+          // truncation / uniform weighting: keys with y = (M - acc) c > W log2 e are outside the
+          // support; inside, exp(s - m) or 1
+          const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
+          const float e0 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x0 * rc.c);
+          const float e1 = UNIF ? 1.0f : __builtin_amdgcn_exp2f(x1 * rc.c);
+          pk = pack_bf16(y0 > rc.cut ? 0.0f : e0, y1 > rc.cut ? 0.0f : e1);
+          if (DUMP) {
+            i0 = y0 > rc.cut ? 254u : 0u;
+            i1 = y1 > rc.cut ? 254u : 0u;
+          }
+        } else if (POT && !FLUSH) {
+          // t = G + (acc - M) c = G - y, rounded to an integer by the FMA itself
+          const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
+          pk = pot_pair(t0, t1, pot_lo);
+          if (DUMP) {
+            i0 = 127u - ((pk >> 7) & 0x1FFu) + (uint32_t)dlag;  // against the running anchor
+            i1 = 127u - ((pk >> 23) & 0x1FFu) + (uint32_t)dlag;
+          }
+        } else if (POT) {  // flush: e >= L -> 0
+          const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
+          const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
+          const uint32_t w0 = b0 < pot_lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
+          const uint32_t w1 = b1 < pot_lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
+          pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+          if (DUMP) {
+            i0 = b0 < pot_lo ? 254u : (uint32_t)(pot_bits - b0 + dlag);
+            i1 = b1 < pot_lo ? 254u : (uint32_t)(pot_bits - b1 + dlag);
+          }
+        } else if (KHARD) {
+          // y = (M - acc) c; t = y + 2^23 rounds y: bits(t) = 0x4B000000 + l, clamped to [0, K]
+          // (the lower clamp keeps the table read inside the row's column when rounding puts
+          // acc a little above M on a very narrow grid)
+          const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
+          const int32_t b0 = min(max((int32_t)fbits(t0), 0x4B000000), 0x4B000000 + L);
+          const int32_t b1 = min(max((int32_t)fbits(t1), 0x4B000000), 0x4B000000 + L);
+          float w0, w1;
+          if (TAB) {  // T_l from the row's column of the table: (bits << SH) drops 0x4B000000
+            w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
+            w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
+          } else {
+            w0 = __builtin_amdgcn_exp2f(rc.step * (float)(b0 - 0x4B000000));
+            w1 = __builtin_amdgcn_exp2f(rc.step * (float)(b1 - 0x4B000000));
+          }
+          const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;
+          if (FLUSH) {  // y > K: below the window
+            w0 = y0 > Kf ? 0.0f : w0;
+            w1 = y1 > Kf ? 0.0f : w1;
+          }
+          pk = pack_bf16(w0, w1);
+          if (DUMP) {
+            i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
+            i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
+          }
+        } else {  // K-interval, interpolation between T_l and T_l+1, l = floor(min(y, K))
+          const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
+          const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
+          const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
+          const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
+          float w0, w1;
+          if (TAB) {  // T_l (1 + t (e^-Delta - 1)); at l = K the parameter t is 0
+            const float T0 = *(const float*)(Tb + ((l0 << SH) + rc.tab));
+            const float T1 = *(const float*)(Tb + ((l1 << SH) + rc.tab));
+            w0 = T0 * fmaf(c0 - f0, rstep, 1.0f);
+            w1 = T1 * fmaf(c1 - f1, rstep, 1.0f);
+          } else {
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            const f2 e0 = kgrid_pair(rc.step, f0), e1 = kgrid_pair(rc.step, f1);  // (T_l, T_l+1 - T_l)
+            w0 = fmaf(c0 - f0, e0.y, e0.x);
+            w1 = fmaf(c1 - f1, e1.y, e1.x);
+          }
+          if (FLUSH) {
+            w0 = y0 > Kf ? 0.0f : w0;
+            w1 = y1 > Kf ? 0.0f : w1;
+          }
+          pk = pack_bf16(w0, w1);
+          if (DUMP) {
+            i0 = (FLUSH && y0 > Kf) ? 254u : l0;
+            i1 = (FLUSH && y1 > Kf) ? 254u : l1;
+          }
+        }
+        if (masked) {
+          const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);  // r0 even: keys k0, k0 + 1
+          const uint32_t m0 = k0 <= lim ? 0x0000FFFFu : 0u, m1 = k0 + 1 <= lim ? 0xFFFF0000u : 0u;
+          pk &= (m0 | m1);
+          if (DUMP) {
+            i0 = k0 <= lim ? i0 : 255u;
+            i1 = k0 + 1 <= lim ? i1 : 255u;
+          }
+        }
+        if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
+          const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);
+          uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
+          if (k0 < N) dst[k0] = (uint8_t)i0;
+          if (k0 + 1 < N) dst[k0 + 1] = (uint8_t)i1;
+        }
+        P[kb][kc][p] = pk;
       }
-      if (RUN) run_anchor(s, o, l, t, last_masked);
-      u32x4 P[2];
-      weights(s[0], 0, P, l, t, last_masked);
-      pv1(t & 1, 0, P, o);
-      weights(s[1], 1, P, l, t, last_masked);
-      pv1(t & 1, 1, P, o);
+  };
+  // a tile's scores are weighed: the running maximum first (online kinds), then both blocks
+  auto fold_max = [&](const f32x16 (&s)[2], int kt, bool masked) __attribute__((always_inline)) {
+    if (WK == WK_EXACT) online_max(s, masked, kt);
+    if (RUN) run_anchor(s, masked, kt);
+  };
+  auto weigh_tile = [&](const f32x16 (&s)[2], int kt, bool masked) __attribute__((always_inline)) {
+    fold_max(s, kt, masked);
+    weights(s[0], 0, kt, masked);
+    weights(s[1], 1, kt, masked);
+  };
+
+  // ---- prologue -----------------------------------------------------------------------------
+  // K(j) sits in K stage j % 2, V(j) in V stage j % 2.  Iteration t multiplies P(t) by V(t),
+  // forms P(t+1) from the scores of tile t+1 and issues the scores of tile t+2; it loads V(t+1)
+  // and K(t+3) into the stages of V(t-1) and K(t+1), both last read in iteration t-1.
+  load_k(0, 0);
+  load_k(min(1, T - 1), 1);
+  load_v(0, 0);
+  loads_done();
+  __syncthreads();  // also publishes the K-interval tables
+  f32x16 sc[2];  // the scores of tile t+1 during iteration t
+  {
+    f32x16 s0[2];
+    if (wlast >= 0) {
+      s0[0] = qk1(0, 0, init);
+      s0[1] = qk1(0, 1, init);
     }
+    if (wlast >= 1) {
+      sc[0] = qk1(1, 0, init);
+      sc[1] = qk1(1, 1, init);
+    }
+    __syncthreads();  // every wave has read K(0) before its stage is refilled
+    load_k(min(2, T - 1), 0);
+    if (wlast >= 0) weigh_tile(s0, 0, wlast == 0 && last_masked);
     loads_done();
-    __syncthreads();
+    lds_barrier();
   }
 
-  // ---- epilogue -----------------------------------------------------------
+  // ---- main loop ----------------------------------------------------------------------------
+  // Every iteration issues the same loads, so the loop needs no branch for them: past the last
+  // tile it reloads tile T-1 into a stage no later iteration reads.
+  int t = 0;
+  auto loads = [&]() __attribute__((always_inline)) {
+    load_v(min(t + 1, T - 1), (t + 1) & 1);
+    load_k(min(t + 3, T - 1), (t + 1) & 1);
+  };
+  // (the index dump's stores count in vmcnt as well: the wait covers them)
+  auto end_iteration = [&]() __attribute__((always_inline)) {
+    loads_done();
+    lds_barrier();
+  };
+  // steady state: tiles t+1 and t+2 hold visible keys for every row and need no mask
+  for (; t + 2 <= wlast && t + 1 < tclean; ++t) {
+    pv(t & 1);
+    loads();
+    if constexpr (WK == WK_EXACT || RUN) {
+      // the online kinds (a running maximum, a rare rescale branch) weigh tile t+1 before they
+      // issue the scores of tile t+2 into the same registers: one score set live, not two
+      weigh_tile(sc, t + 1, false);
+      sc[0] = qk1(t & 1, 0, init);  // K(t+2) is in stage (t+2) % 2
+      sc[1] = qk1(t & 1, 1, init);
+    } else {
+      const f32x16 n0 = qk1(t & 1, 0, init);
+      weights(sc[0], 0, t + 1, false);
+      weights(sc[1], 1, t + 1, false);
+      const f32x16 n1 = qk1(t & 1, 1, init);
+      sc[0] = n0;
+      sc[1] = n1;
+    }
+    end_iteration();
+  }
+  // the last tiles of the wave (the last may need masking), then the iterations in which the
+  // wave only issues its share of the other waves' tile loads
+  for (; t < T; ++t) {
+    if (t <= wlast) pv(t & 1);
+    loads();
+    if (t + 1 <= wlast) weigh_tile(sc, t + 1, t + 1 >= tclean);
+    if (t + 2 <= wlast) {  // (the scores of tile t+2 reuse the registers of tile t+1's)
+      sc[0] = qk1(t & 1, 0, init);
+      sc[1] = qk1(t & 1, 1, init);
+    }
+    end_iteration();
+  }
+
+  // ---- epilogue -----------------------------------------------------------------------------
   if (wlast < 0) return;
-  const float lt = half_sum(l);
+  // the selector MMA left the sum of query n (n + 16) in lane n (n + 32), register 0
+  const float lt = bitsf(__builtin_amdgcn_ds_bpermute(4 * (li < 16 ? li : li + 16), (int)fbits(rs[0])));
   if (DUMP && row >= a.idx_row0 && row < a.idx_row0 + a.idx_rows && row < N) {
     uint8_t* dst = a.grid_idx + ((size_t)bh * a.idx_rows + (row - a.idx_row0)) * N;
     for (int key = (wlast + 1) * BN + hh; key < N; key += 2) dst[key] = 255u;  // beyond the wave's last tile
@@ -508,26 +529,236 @@ __global__ __launch_bounds__(NW * 64, QSA_BF16_WAVES_PER_SIMD) void fwd_bf16(Fwd
 #endif
 }
 
-template <int D, int WK>
-hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
-  FwdArgs a = a0;
-  a.n_qtiles = (a.N + BM - 1) / BM;
-  a.total_blocks = a.B * a.H * a.n_qtiles;
-  // No K-interval table: the weights evaluate T_l = 2^(l step) from the grid index (one
-  // v_exp_f32 per element, interpolation two).  In bf16 that measured 25-33 % faster than the
-  // per-element LDS gather from a per-row table, which also cost LDS space; the fp8 kernel,
-  // whose loop is bound by VALU issue, keeps the table (there the evaluated form was slower).
-  const size_t lds = 2 * (size_t)BN * ((D / 8 + 1) + (D / 8 + 4)) * 16;
-  const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true> : (const void*)fwd_bf16<D, WK, false>;
+// ---- row-extrema pre-pass with two row blocks per wave ----------------------------------
+// The row maximum (and minimum) over the visible keys of every query row, from the same MMAs
+// in the same order as the main kernel's score tiles (zero-initialised).  A wave owns XRB = 2
+// blocks of 32 rows, so every K operand read from LDS feeds two MMAs; the scores of tile t+1
+// are issued before the extrema of tile t are folded.  The extrema are parked in O where
+// fwd_bf16 reads them.
+constexpr int XNW = 4;               // waves per workgroup
+constexpr int XRB = 2;               // 32-row blocks per wave
+constexpr int XBM = XNW * 32 * XRB;  // query rows per workgroup
+constexpr int XNB = 2;               // K tile buffers
+
+template <int D, bool TMIN>
+__global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KC = D / 16;
+  using LY = Lay<D>;
+  constexpr int SL = LY::SL, RR = LY::RR, KT = LY::KT;
+  constexpr int KIW = SL / XNW;  // K-tile load instructions per wave
+  static_assert(SL % XNW == 0, "K tiles split evenly over the waves");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  lds_u8* const lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hh = lane >> 5;
+  int bh, qt;
+  map_block(a, bh, qt);
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int kvh = h / (a.H / a.Hkv);
+  const int N = a.N;
+  const int q0 = qt * XBM;
+  const int wr0 = q0 + wave * 32 * XRB;
+  const __bf16* Qg = (const __bf16*)a.q + (size_t)(b * a.H + h) * N * D;
+  const __bf16* const Kg = (const __bf16*)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
+
+  u32x4 qf[XRB][KC];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const int row = wr0 + 32 * rb + li;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qf[rb][c] = row < N ? *(const u32x4*)(Qg + (size_t)row * D + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
+  }
+
+  const int T = a.causal ? ((min(q0 + XBM, N) - 1) / BN + 1) : (N + BN - 1) / BN;
+  int last[XRB];
+  bool lmask[XRB];
+  int tclean = T;  // tiles t < tclean are visible and unmasked for every row block of the wave
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const int r0 = wr0 + 32 * rb;
+    last[rb] = r0 >= N ? -1 : (a.causal ? (min(r0 + 31, N - 1) / BN) : T - 1);
+    lmask[rb] = (a.causal && last[rb] * BN + BN - 1 > r0) || (last[rb] * BN + BN > N);
+    tclean = min(tclean, lmask[rb] ? last[rb] : last[rb] + 1);
+  }
+  const int wlast = max(last[0], last[1]);
+
+  // K tiles as in fwd_bf16: slot s (64 per wave instruction) is row j = s / SL, position
+  // s % SL of the row, which holds chunk (s % SL) ^ kswz(j)
+  uint32_t kvo[KIW];
+#pragma unroll
+  for (int m = 0; m < KIW; ++m) {
+    const int sl = (wave + XNW * m) * 64 + lane, j = sl / SL, c = sl % SL;
+    kvo[m] = (uint32_t)(j * D + 8 * (c ^ kswz_of<D>(j))) * 2;
+  }
+  auto load_k = [&](int kt, int buf) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kt * BN * D), 0, (N - kt * BN) * D * 2, 0x00020000);
+#pragma unroll
+    for (int m = 0; m < KIW; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + buf * KT + (wave + XNW * m) * 1024), 16, kvo[m], 0, 0, 0);
+  };
+
+  uint32_t koff[KC];  // chunk 2c + hh of K row li at its swizzled slot
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = li * RR + 16 * ((2 * c + hh) ^ kswz_of<D>(li));
+  const f32x16 zero16 = {};
+  // scores of tile buf for both row blocks: s[rb][kb] = 32 keys kb x 32 rows rb (S^T)
+  auto qk = [&](int buf, f32x16 (&s)[XRB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const lds_u8* kbase = lds + buf * KT + kb * 32 * RR;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 ka = *(const lds_u32x4*)(kbase + koff[c]);
+#pragma unroll
+        for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma(ka, qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+      }
+    }
+  };
+  float M[XRB], MN[XRB];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    M[rb] = -__builtin_inff();
+    MN[rb] = __builtin_inff();
+  }
+  auto fold = [&](int rb, const f32x16 (&s)[2], int kt, bool masked) {
+    const int row = wr0 + 32 * rb + li;
+    const int lim = a.causal ? min(row, N - 1) : N - 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = !masked || kt * BN + kb * 32 + acc_key(r, hh) <= lim;
+        M[rb] = fmaxf(M[rb], ok ? s[kb][r] : -__builtin_inff());
+        if (TMIN) MN[rb] = fminf(MN[rb], ok ? s[kb][r] : __builtin_inff());
+      }
+  };
+  auto fold_all = [&](const f32x16 (&s)[XRB][2], int t) {
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) {
+      if (t < last[rb]) fold(rb, s[rb], t, false);
+      else if (t == last[rb]) fold(rb, s[rb], t, lmask[rb]);
+    }
+  };
+
+  for (int j = 0; j < XNB; ++j)
+    if (j < T) load_k(j, j);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 s[XRB][2];
+  if (wlast >= 0) qk(0, s);
+  __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+  int kl = 0, kn = 1;  // buffers of K(t) and K(t+1)
+  int t = 0;
+  auto end_iteration = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(t+2), this iteration's load
+    __syncthreads();
+    kl = kn;
+    kn = kn + 1 == XNB ? 0 : kn + 1;
+  };
+  // steady state: tile t is unmasked for both row blocks and tile t+1 is needed.  Unrolled by
+  // two so that the score sets swap roles instead of being copied.
+  auto step = [&](const f32x16 (&cur)[XRB][2], f32x16 (&nxt)[XRB][2]) {
+    if (t + XNB < T) load_k(t + XNB, kl);  // buffer of K(t), last read in iteration t-1
+    qk(kn, nxt);
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) fold(rb, cur[rb], t, false);
+    end_iteration();
+  };
+  f32x16 s2[XRB][2];
+  for (; t + 2 < tclean; t += 2) {
+    step(s, s2);
+    ++t;
+    step(s2, s);
+    --t;
+  }
+  if (t + 1 < tclean) {
+    step(s, s2);
+#pragma unroll
+    for (int rb = 0; rb < XRB; ++rb) {
+      s[rb][0] = s2[rb][0];
+      s[rb][1] = s2[rb][1];
+    }
+    ++t;
+  }
+  for (; t < T; ++t) {
+    if (t + XNB < T) load_k(t + XNB, kl);
+    if (t < wlast) {
+      f32x16 sn[XRB][2];
+      qk(kn, sn);
+      fold_all(s, t);
+#pragma unroll
+      for (int rb = 0; rb < XRB; ++rb) {
+        s[rb][0] = sn[rb][0];
+        s[rb][1] = sn[rb][1];
+      }
+    } else if (t == wlast) {
+      fold_all(s, t);
+    }
+    end_iteration();
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    const float m = half_max(M[rb]);
+    const float mn = half_min(MN[rb]);
+    const int r0 = wr0 + 32 * rb;
+    // packed at the start of the 32-row block's slice of O, where fwd_bf16 reads them
+    uint32_t* const park = (uint32_t*)((__bf16*)a.o + ((size_t)bh * N + r0) * D) + 2 * li;
+    if (hh == 0 && r0 + li < N) {
+      park[0] = fbits(m);
+      park[1] = fbits(mn);
+    }
+  }
+#endif
+}
+
+template <int D, int WK, bool TAB>
+hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
+  // the table holds T_l alone for both hard rounding and interpolation
+  const size_t lds = (size_t)Lay<D>::TAB + (TAB ? (size_t)BM * (a.levels + 1) * 4 : 0);
+  const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true, TAB> : (const void*)fwd_bf16<D, WK, false, TAB>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_bf16<D, WK, true>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_bf16<D, WK, true, TAB>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((fwd_bf16<D, WK, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_bf16<D, WK, false, TAB>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
+}
+
+template <int D, int WK>
+hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
+  FwdArgs a = a0;
+  a.n_qtiles = (a.N + BM - 1) / BM;
+  a.total_blocks = a.B * a.H * a.n_qtiles;
+  constexpr bool ANCH = WK != WK_EXACT && !wk_running(WK);
+  if constexpr (ANCH) {  // the row-extrema pre-pass, on its own workgroup grid
+    FwdArgs x = a0;
+    x.n_qtiles = (x.N + XBM - 1) / XBM;
+    x.total_blocks = x.B * x.H * x.n_qtiles;
+    const size_t xl = (size_t)XNB * Lay<D>::KT;  // K tile buffers only
+    if (x.track_min)
+      hipLaunchKernelGGL((rowext_bf16<D, true>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
+    else
+      hipLaunchKernelGGL((rowext_bf16<D, false>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // K-interval grid values: from a per-row table in LDS while it fits (K <= 16), else evaluated
+  // per element as 2^(l step) (one v_exp_f32, two for interpolation)
+  if constexpr (wk_kint(WK)) {
+    if (a.levels <= KTAB_MAX) return launch_main<D, WK, true>(a, st);
+  }
+  return launch_main<D, WK, false>(a, st);
 }
 
 template <int D>

@@ -35,6 +35,12 @@ __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
                                                   0, 0, 0);
 }
 
+// 16x16x32 bf16 MMA (the row sums of a P^T operand against a 0/1 selector)
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
 // 32x32x64 8-bit MMA: A in OCP fp8 e4m3, B in e4m3 (fmt_b = 0) or bf8 e5m2 (fmt_b = 1).
 template <int FMT_B>
 __device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {

@@ -168,11 +168,13 @@ template <> struct Weight<WK_UNIF> : SupportW<true> {};
 
 // Per-row constants from the pre-pass extrema (raw units) and, for
 // K-interval, the row's grid table written into LDS (unless `tab` is null:
-// the bf16 kernel evaluates T_l = 2^(l step) from the index with the same
-// instruction instead, which gives the same values without the table).  The
-// K+1 table entries are split between the `nsplit` lanes that share a row
-// (this lane writes entries part, part + nsplit, ...).
-template <int WK, int SH>
+// the weights then evaluate T_l = 2^(l step) from the index with the same
+// instruction, which gives the same values without the table).  The K+1
+// table entries are split between the `nsplit` lanes that share a row (this
+// lane writes entries part, part + nsplit, ...).  TONLY: the interpolation
+// table holds T_l alone, like the hard-rounding one (the kernel forms T_l+1
+// from T_l), instead of the pairs (T_l, T_l+1 - T_l).
+template <int WK, int SH, bool TONLY = false>
 __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, int row_local,
                                          unsigned char* tab, int part, int nsplit) {
   RowC rc;
@@ -197,7 +199,7 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
   rc.mc = M * rc.c;
   const float step = -delta_s * kLog2e;
   rc.step = step;
-  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH);
+  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH) && !TONLY;
   constexpr int ROWS = (1 << SH) / 4;
   rc.tab = (uint32_t)row_local * (INTERP ? 8u : 4u);
   if (tab == nullptr) return rc;
