@@ -31,6 +31,13 @@
 namespace qsa {
 namespace {
 
+// Ablation build only (-DQSA_FP8_POT_PV16=1): Rowmax-PoT with the pre-pass runs the bf16 PV path
+// of the exact kinds (bf16 weights built from the exponent field, V widened to bf16), so that
+// its time against the exact kinds separates the exponential from the 8-bit PV product.
+#ifndef QSA_FP8_POT_PV16
+#define QSA_FP8_POT_PV16 0
+#endif
+
 constexpr int NW = 4;    // waves per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int BM = 128;  // query rows per workgroup
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr bool KHARD = (WK == WK_KH || WK == WK_KH_FLUSH);
   constexpr bool SUPPORT = wk_support(WK), UNIF = (WK == WK_UNIF);
   constexpr bool FLUSH = (WK == WK_POT_FLUSH || WK == WK_POTR_FLUSH || WK == WK_KH_FLUSH || WK == WK_KI_FLUSH);
-  constexpr bool PV8 = POT;
+  constexpr bool PV8 = POT && !(QSA_FP8_POT_PV16 && !RUN);
   constexpr int SK = D / 16;                          // 16-byte slots per K row (swizzled)
   constexpr int SV = PV8 ? D / 16 : (D / 8 + 4);  // fp8 V rows (swizzled, unpadded), or bf16 rows (stride 64 mod 256)
   constexpr int KR = SK * 16, VR = SV * 16;
@@ -361,6 +368,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
           if (DUMP) {
             i0 = y0 > rc.cut ? 254u : 0u;
             i1 = y1 > rc.cut ? 254u : 0u;
+          }
+        } else if (POT) {
+          // (ablation build: PoT weights as bf16 exponent fields, as in the bf16 kernel)
+          const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
+          const int32_t lo = pot_bits - (L - 1);
+          if (!FLUSH) {
+            pk = pot_pair(t0, t1, lo);
+            if (DUMP) {
+              i0 = 127u - ((pk >> 7) & 0x1FFu);
+              i1 = 127u - ((pk >> 23) & 0x1FFu);
+            }
+          } else {
+            const int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
+            const uint32_t w0 = b0 < lo ? 0u : (((uint32_t)b0 << 23) + (127u << 23));
+            const uint32_t w1 = b1 < lo ? 0u : (((uint32_t)b1 << 23) + (127u << 23));
+            pk = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+            if (DUMP) {
+              i0 = b0 < lo ? 254u : (uint32_t)(pot_bits - b0);
+              i1 = b1 < lo ? 254u : (uint32_t)(pot_bits - b1);
+            }
           }
         } else if (KHARD) {
           const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
@@ -902,7 +929,7 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   FwdArgs a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.total_blocks = a.B * a.H * a.n_qtiles;
-  constexpr bool PV8 = wk_pot(WK);
+  constexpr bool PV8 = wk_pot(WK) && !(QSA_FP8_POT_PV16 && !wk_running(WK));
   constexpr bool ANCH = WK != WK_EXACT && !wk_running(WK);
   constexpr int SK = D / 16, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
