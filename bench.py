@@ -277,8 +277,8 @@ BWD_FLOPS_PER_PAIR_D = 10   # algorithmic backward: S recompute, dP, dV, dK, dQ 
 
 
 def bwd_executed_flops_per_pair(d):
-    """fp32 FMA work the three backward launches execute per visible pair (2 flops per FMA):
-    rows S twice and dP once; keys S, dP, dV, dK; dQ S, dP, dQ."""
+    """Matrix-core work the three backward launches execute per visible pair (2 flops per
+    multiply-add): rows S twice and dP once; keys S, dP, dV, dK; dQ S, dP, dQ."""
     return 2 * d * (3 + 4 + 3)
 
 
@@ -310,7 +310,7 @@ def cpu_baseline_bwd(wl, x, do, var, grad, budget_s):
 
 
 def backward_run(args):
-    """The attention backward (qsa_attn_bwd: three fp32 launches) on the GPT-2-small shaped
+    """The attention backward (qsa_attn_bwd: three bf16 matrix-core launches) on the GPT-2-small shaped
     pretraining attention (B 8, H 12, N 1024, d 64, bf16, causal), K-interval K = 4 with min-max
     calibration and hard rounding through the pre-normalisation surrogate, plus a table of
     other kinds and gradient modes."""
@@ -330,16 +330,17 @@ def backward_run(args):
     rec = {
         "metric": "attention bwd TFLOP/s (credited 10 d flops per visible pair)", "value": round(tflops, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "Hkv": x.k.shape[1], "N": N, "d": d, "causal": wl.causal,
                    "inputs": "bf16", "variant": head[0], "grad": head[1], "parallelism": "single GPU"},
         "wall_s_timed_region": round(wall, 4),
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS["f32"], 4), "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_TFLOPS["bf16"], 4), "traffic": None,
                      "flops_per_launch": credited, "flops_per_pair": BWD_FLOPS_PER_PAIR_D * d,
                      "executed_flops_per_pair": bwd_executed_flops_per_pair(d),
                      "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 3),
-                     "note": "the three launches of one call timed together (HIP events); fp32 vector FMA peak"},
+                     "note": "the three launches of one call timed together (HIP events); dense bf16 MFMA peak "
+                             "(operands bf16, accumulation and every weight and gradient step in float32)"},
     }
     table = {}
     for name, var, grad in [("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_post"),

@@ -425,9 +425,10 @@ def _weight_partials(rw, kind, levels, interp, flush, visible, window, ste=False
 
 
 def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window=None, interp=False,
-             flush=False, scale=None, grad="ste_post", extrema=None):
+             flush=False, scale=None, grad="ste_post", extrema=None, detail=False):
     """Gradients for one (batch, head): qh (N, d), kh/vh (N, d), doh (N, d) float64.
-    Returns dict dQ (N, d), dK (N, d), dV (N, d) (this head's share of dK, dV).
+    Returns dict dQ (N, d), dK (N, d), dV (N, d) (this head's share of dK, dV); with
+    ``detail`` also the normalised weights P and the score gradients dS (N, N) they come from.
     ``extrema`` (detached modes only) = (m, mn) per row, as in row_weights."""
     if grad not in GRADS:
         raise ValueError(f"unknown gradient mode {grad!r}")
@@ -493,7 +494,10 @@ def head_bwd(qh, kh, vh, doh, *, causal=False, kind="exact", levels=None, window
                 np.add.at(dS, (rows, amin), dlo)
     dQ = sc * (dS @ kh)
     dK = sc * (dS.T @ qh)
-    return {"dQ": dQ, "dK": dK, "dV": dV}
+    out = {"dQ": dQ, "dK": dK, "dV": dV}
+    if detail:
+        out.update(P=P, dS=dS)
+    return out
 
 
 def attn_bwd(q, k, v, do, *, causal=False, kind="exact", levels=None, window=None, interp=False, flush=False,

@@ -70,5 +70,6 @@ hipError_t launch_bf16(const FwdArgs& a, int d, int wk, hipStream_t s);
 hipError_t launch_fp8(const FwdArgs& a, int d, int wk, hipStream_t s);
 hipError_t launch_f32(const FwdArgs& a, int d, int wk, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int d, int wk, hipStream_t s);
+hipError_t launch_bwd_mma(const BwdArgs& a, int d, int wk, hipStream_t s);  // bf16 inputs, matrix cores
 
 }  // namespace qsa

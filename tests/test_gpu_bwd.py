@@ -1,5 +1,5 @@
-"""GPU parity of the attention backward (qsa_attn_bwd, float32 arithmetic) against the
-oracle's float64 backward, element by element on dQ, dK and dV.
+"""GPU parity of the attention backward (qsa_attn_bwd) against the oracle's float64 backward,
+element by element on dQ, dK and dV.
 
 Inputs: seeded Q, K, V (inputs.make_inputs) and dO (inputs.make_dout) in the stored dtype;
 the oracle takes the same stored values, decoded exactly.  The quantized weights are piecewise
@@ -11,6 +11,13 @@ comparison is exact-decision everywhere else.  Tolerance: max |gpu - oracle| <= 
 max(max |oracle|, FLOOR) per tensor (float32 sums of at most N terms; the floor covers
 gradients that vanish exactly, as with a single visible key, where float32 leaves rounding
 residue of order 1e-8 on inputs of order 1).
+
+bf16 inputs run on the matrix cores, which take the normalised weights P and the score
+gradients dS rounded to bfloat16 (nearest even, relative error at most u = 2^-8) as the operands
+of dV = P^T dO, dK = scale dS^T Q and dQ = scale dS K.  Rounding the operand of a sum of products
+moves it by at most u times the sum of the absolute products, so each element also gets
+(u + 2^-12) * (|P|^T |dO|, scale |dS|^T |Q|, scale |dS| |K|) on top of the float32 tolerance (the
+2^-12 covers float32 accumulation over the row or column).
 """
 from __future__ import annotations
 
@@ -31,6 +38,7 @@ EDGE_Y = 2e-4     # grid-coordinate units
 EDGE_S = 2e-5     # score units
 TOL = 2e-4
 FLOOR = 1e-3
+BF16_U = 2.0 ** -8 + 2.0 ** -12   # bfloat16 unit roundoff of the P and dS operands, plus fp32 accumulation
 MODES = ["ste_post", "ste_pre", "ste_pre_detached", "exact", "exact_detached"]
 KINDS = [gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.POT4F, gc.KH4, gc.KH16, gc.KI4, gc.KI16, gc.KH4W, gc.KI4W, gc.KH4WF,
          gc.KI4WF, gc.TRUNC2, gc.UNIF2]
@@ -104,19 +112,28 @@ def _case(wl, var, grad, heads=None):
     torch.cuda.synchronize()
     dq, dk, dv = (t.cpu().numpy() for t in (dq, dk, dv))
     worst = {}
+    mma = wl.dtype == "bf16"   # the matrix-core path: bf16 P and dS operands
     for b in bs:
         oq = np.zeros((H, N, d))
         ok_ = np.zeros((Hkv, N, d))
         ov = np.zeros((Hkv, N, d))
+        bq, bk, bv = np.zeros((H, N, d)), np.zeros((Hkv, N, d)), np.zeros((Hkv, N, d))
         for h in range(H):
-            r = oracle.head_bwd(qf[b, h], kf[b, h // group], vf[b, h // group], dof[b, h], causal=wl.causal,
-                                grad=grad, **ovar)
-            oq[h], ok_[h // group], ov[h // group] = r["dQ"], ok_[h // group] + r["dK"], ov[h // group] + r["dV"]
+            kv = h // group
+            r = oracle.head_bwd(qf[b, h], kf[b, kv], vf[b, kv], dof[b, h], causal=wl.causal, grad=grad, detail=mma,
+                                **ovar)
+            oq[h], ok_[kv], ov[kv] = r["dQ"], ok_[kv] + r["dK"], ov[kv] + r["dV"]
+            if mma:
+                aS, aP = np.abs(r["dS"]), np.abs(r["P"])
+                bq[h] = BF16_U * sc * (aS @ np.abs(kf[b, kv]))
+                bk[kv] += BF16_U * sc * (aS.T @ np.abs(qf[b, h]))
+                bv[kv] += BF16_U * (aP.T @ np.abs(dof[b, h]))
         hs = sorted({h for bb, h in heads if bb == b})
         kvs = sorted({h // group for h in hs})
-        for name, got, ref in (("dQ", dq[b][hs], oq[hs]), ("dK", dk[b][kvs], ok_[kvs]), ("dV", dv[b][kvs], ov[kvs])):
+        for name, got, ref, bnd in (("dQ", dq[b][hs], oq[hs], bq[hs]), ("dK", dk[b][kvs], ok_[kvs], bk[kvs]),
+                                    ("dV", dv[b][kvs], ov[kvs], bv[kvs])):
             scale = max(np.abs(ref).max(), FLOOR)
-            err = np.abs(got - ref).max() / scale
+            err = np.max(np.maximum(np.abs(got - ref) - bnd, 0.0)) / scale
             worst[name] = max(worst.get(name, 0.0), err)
     print(f"[bwd]   rel err " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in worst.items()), flush=True, file=sys.stderr)
     for name, err in worst.items():

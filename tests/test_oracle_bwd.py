@@ -71,6 +71,23 @@ def test_straight_through_equals_autograd_construction(var, causal):
     np.testing.assert_allclose(r["dV"], V.grad.numpy(), atol=1e-12)
 
 
+@pytest.mark.parametrize("var", KINDS[:6], ids=_vid)
+@pytest.mark.parametrize("causal", [False, True])
+def test_detail_weights_and_score_gradients_equal_autograd_at_the_scores(var, causal):
+    """``detail``: P and dS are the normalised weights and the gradient of the loss with
+    respect to the scaled scores, here with the scores as the autograd leaf (ste_post)."""
+    q, k, v, do = _qkvdo(N=10, d=4, sigma=1.6, seed=3)
+    d = q.shape[3]
+    r = oracle.head_bwd(q[0, 1], k[0, 0], v[0, 0], do[0, 1], causal=causal, grad="ste_post", detail=True, **var)
+    S = torch.tensor(q[0, 1] @ k[0, 0].T / math.sqrt(d), requires_grad=True)
+    w = oracle.head_rows(q[0, 1], k[0, 0], v[0, 0], causal=causal, detail=True, **var)["w"]
+    logw = torch.from_numpy(np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf))
+    P = torch.softmax(S + (logw - S).detach(), dim=-1)
+    ((P @ torch.from_numpy(v[0, 0])) * torch.from_numpy(do[0, 1])).sum().backward()
+    np.testing.assert_allclose(r["P"], P.detach().numpy(), atol=1e-14)
+    np.testing.assert_allclose(r["dS"], S.grad.numpy(), atol=1e-12)
+
+
 LOG2E = 1.0 / math.log(2.0)
 
 
