@@ -276,6 +276,15 @@ def energy_run(args):
 BWD_FLOPS_PER_PAIR_D = 10   # algorithmic backward: S recompute, dP, dV, dK, dQ (2 d flops each per pair)
 
 
+BWD_TABLE = [("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_post"),
+             ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_pre_detached"),
+             ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "exact"),
+             ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True}, "ste_pre"),
+             ("kint4_window8_hard", {"kind": "kint", "levels": 4, "window": 8.0}, "ste_post"),
+             ("pot8", {"kind": "pot", "levels": 8}, "ste_pre"),
+             ("exact", {"kind": "exact"}, "ste_post")]
+
+
 def bwd_executed_flops_per_pair(d):
     """Matrix-core work the three backward launches execute per visible pair (2 flops per
     multiply-add): rows S twice and dP once; keys S, dP, dV, dK; dQ S, dP, dQ."""
@@ -324,6 +333,9 @@ def backward_run(args):
     fn = lambda var, grad: qsa.attn_bwd(q, k, v, g, causal=wl.causal, grad=grad, **var)  # noqa: E731
     print("[bwd] timing the headline", file=sys.stderr, flush=True)
     ms, wall = time_loop(lambda: fn(*head), args.steps, args.warmup)
+    if args.only_kernel:
+        print(json.dumps({"ms_per_call": ms}))
+        return 0
     credited = BWD_FLOPS_PER_PAIR_D * d * P
     tflops = credited / (ms * 1e-3) / 1e12
     executed = bwd_executed_flops_per_pair(d) * P
@@ -343,21 +355,15 @@ def backward_run(args):
                              "(operands bf16, accumulation and every weight and gradient step in float32)"},
     }
     table = {}
-    for name, var, grad in [("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_post"),
-                            ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "ste_pre_detached"),
-                            ("kint4_minmax_hard", {"kind": "kint", "levels": 4}, "exact"),
-                            ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True},
-                             "ste_pre"),
-                            ("kint4_window8_hard", {"kind": "kint", "levels": 4, "window": 8.0}, "ste_post"),
-                            ("pot8", {"kind": "pot", "levels": 8}, "ste_pre"),
-                            ("exact", {"kind": "exact"}, "ste_post")]:
+    for name, var, grad in [] if args.no_variants else BWD_TABLE:
         print(f"[bwd] {name} {grad}", file=sys.stderr, flush=True)
         t, host = time_calls(lambda: fn(var, grad), args.variant_calls // 4 or 5)
         med = float(np.median(t))
         table[f"{name}:{grad}"] = {"median_ms": round(med, 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
                                    "p90_ms": round(float(np.percentile(t, 90)), 5), "host_call_ms": round(host, 5),
                                    "tflops": round(credited / (med * 1e-3) / 1e12, 3)}
-    rec["variants"] = table
+    if table:
+        rec["variants"] = table
     if not args.no_cpu_baseline:
         print("[bwd] oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline_bwd(wl, x, do, head[0], head[1], args.cpu_seconds)

@@ -270,7 +270,11 @@ enum {
  *   stream       hipStream_t or NULL.
  * dQ, dK and dV must not overlap each other or the inputs.  The forward's O is
  * not needed: the call recomputes the weights from Q and K (three kernels on
- * `stream`).  Float32 arithmetic throughout.  Returns a qsa_status.
+ * `stream`).  Float32 inputs: float32 arithmetic throughout.  BFloat16 inputs:
+ * the products run on the matrix cores with float32 accumulation, and the
+ * normalised weights P and score gradients dS enter dV = P^T dO, dK = scale
+ * dS^T Q and dQ = scale dS K rounded to bfloat16; every weight and gradient
+ * step between the products is float32.  Returns a qsa_status.
  */
 int qsa_attn_bwd(const void* Q, const void* K, const void* V, const void* dO,
                  float* dQ, float* dK, float* dV,

@@ -35,8 +35,9 @@ int validate(int B, int H, int Hkv, int N, int d, int causal, int variant, int k
   if (N > (1 << 20)) return fail(QSA_ERR_SHAPE, "N=%d exceeds 2^20", N);
   if (d < 1) return fail(QSA_ERR_SHAPE, "d=%d must be >= 1", d);
   if (d != 64 && d != 128) return fail(QSA_ERR_UNSUPPORTED, "head dimension d=%d: only 64 and 128 are built", d);
-  if ((int64_t)B * H * N * d >= (int64_t(1) << 31) || (int64_t)B * Hkv * N * d >= (int64_t(1) << 31))
-    return fail(QSA_ERR_SHAPE, "tensor has 2^31 or more elements");
+  // B * H * N * d < 2^31, tested as B * H <= (2^31 - 1) / (N * d) so that no product overflows
+  const int64_t per_head = (int64_t)N * d, cap = ((int64_t(1) << 31) - 1) / per_head;
+  if ((int64_t)B * H > cap || (int64_t)B * Hkv > cap) return fail(QSA_ERR_SHAPE, "tensor has 2^31 or more elements");
   if (dtype != QSA_DT_F32 && dtype != QSA_DT_BF16 && dtype != QSA_DT_FP8_E4M3)
     return fail(QSA_ERR_PARAM, "unknown dtype %d", dtype);
   const int base = variant & QSA_BASE_MASK;

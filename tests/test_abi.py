@@ -210,3 +210,25 @@ def test_backward_binding_rejects_bad_tensors_on_host():
         qsa.attn_bwd(q, q, q, q)                      # CPU tensors
     with pytest.raises(ValueError):
         qsa.attn_bwd(q, q, q, q, grad="nope")         # unknown mode
+
+
+def test_host_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The host layer (qsa_api.cpp) built by g++ with ASan + UBSan against stub launchers
+    (tests/host/abi_host_check.cpp) and driven through every validation branch, the argument
+    marshalling and the error reporting; any sanitizer report aborts the run."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir("/opt/rocm/include/hip"):
+        pytest.skip("needs g++ and the HIP headers")
+    exe = str(tmp_path / "abi_host_check")
+    csrc = os.path.join(ROOT, "quantized_softmax_approximation_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+           "-I" + csrc, os.path.join(csrc, "qsa_api.cpp"), os.path.join(ROOT, "tests", "host", "abi_host_check.cpp"),
+           "-pthread", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("host checks passed"), (r.stdout + r.stderr)[-4000:]
