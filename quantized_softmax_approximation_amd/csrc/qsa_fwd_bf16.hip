@@ -529,21 +529,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
 #endif
 }
 
-// ---- row-extrema pre-pass with two row blocks per wave ----------------------------------
+// ---- row-extrema pre-pass ---------------------------------------------------------------
 // The row maximum (and minimum) over the visible keys of every query row, from the same MMAs
-// in the same order as the main kernel's score tiles (zero-initialised).  A wave owns XRB = 2
-// blocks of 32 rows, so every K operand read from LDS feeds two MMAs; the scores of tile t+1
-// are issued before the extrema of tile t are folded.  The extrema are parked in O where
-// fwd_bf16 reads them.
-constexpr int XNW = 4;               // waves per workgroup
-constexpr int XRB = 2;               // 32-row blocks per wave
-constexpr int XBM = XNW * 32 * XRB;  // query rows per workgroup
-constexpr int XNB = 2;               // K tile buffers
+// in the same order as the main kernel's score tiles (zero-initialised).  A wave owns XRB
+// blocks of 32 rows: with two, every K operand read from LDS feeds two MMAs; with one, a
+// workgroup covers half the rows, so a small grid has twice the workgroups and its longest
+// (causal, last) row block half the serial MMA chain.  The scores of tile t+1 are issued
+// before the extrema of tile t are folded.  The extrema are parked in O where fwd_bf16 reads
+// them.
+constexpr int XNW = 4;  // waves per workgroup
+constexpr int XNB = 2;  // K tile buffers
+constexpr int xbm(int xrb) { return XNW * 32 * xrb; }  // query rows per workgroup
 
-template <int D, bool TMIN>
+template <int D, bool TMIN, int XRB>
 __global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int KC = D / 16;
+  constexpr int KC = D / 16, XBM = xbm(XRB);
   using LY = Lay<D>;
   constexpr int SL = LY::SL, RR = LY::RR, KT = LY::KT;
   constexpr int KIW = SL / XNW;  // K-tile load instructions per wave
@@ -585,7 +586,9 @@ __global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
     lmask[rb] = (a.causal && last[rb] * BN + BN - 1 > r0) || (last[rb] * BN + BN > N);
     tclean = min(tclean, lmask[rb] ? last[rb] : last[rb] + 1);
   }
-  const int wlast = max(last[0], last[1]);
+  int wlast = last[0];
+#pragma unroll
+  for (int rb = 1; rb < XRB; ++rb) wlast = max(wlast, last[rb]);
 
   // K tiles as in fwd_bf16: slot s (64 per wave instruction) is row j = s / SL, position
   // s % SL of the row, which holds chunk (s % SL) ^ kswz(j)
@@ -742,14 +745,21 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   a.total_blocks = a.B * a.H * a.n_qtiles;
   constexpr bool ANCH = WK != WK_EXACT && !wk_running(WK);
   if constexpr (ANCH) {  // the row-extrema pre-pass, on its own workgroup grid
+    // two row blocks per wave unless that leaves fewer workgroups than two per CU
     FwdArgs x = a0;
-    x.n_qtiles = (x.N + XBM - 1) / XBM;
+    const int q2 = (x.N + xbm(2) - 1) / xbm(2);
+    const bool one = (long)x.B * x.H * q2 < 512;
+    x.n_qtiles = one ? (x.N + xbm(1) - 1) / xbm(1) : q2;
     x.total_blocks = x.B * x.H * x.n_qtiles;
     const size_t xl = (size_t)XNB * Lay<D>::KT;  // K tile buffers only
-    if (x.track_min)
-      hipLaunchKernelGGL((rowext_bf16<D, true>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
-    else
-      hipLaunchKernelGGL((rowext_bf16<D, false>), dim3(x.total_blocks), dim3(XNW * 64), xl, st, x);
+    const dim3 g(x.total_blocks), t(XNW * 64);
+    if (x.track_min) {
+      if (one) hipLaunchKernelGGL((rowext_bf16<D, true, 1>), g, t, xl, st, x);
+      else hipLaunchKernelGGL((rowext_bf16<D, true, 2>), g, t, xl, st, x);
+    } else {
+      if (one) hipLaunchKernelGGL((rowext_bf16<D, false, 1>), g, t, xl, st, x);
+      else hipLaunchKernelGGL((rowext_bf16<D, false, 2>), g, t, xl, st, x);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
