@@ -331,6 +331,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   int32_t pot_lo = pot_bits - ec;                                       // bits of G - ec
   const uint32_t pot_add = 0x00010001u * (uint32_t)(4 * L * 257);     // 4L in both bytes of a half
   const float Kf = (float)a.levels;
+  const float kt_hi = 8388608.0f + Kf;  // 2^23 + K
   // Single-pass PoT: A = ceil(running max of s log2 e), an integer.  The weights are formed
   // against a lagging integer anchor Aw <= A (tb = G - Aw, so the FMA below rounds
   // G - (Aw - s log2 e) = G - e_w), with the clip moved by the lag dl = A - Aw: e_w <= ec - dl,
@@ -391,9 +392,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
           }
         } else if (KHARD) {
           const float t0 = fmaf(x0, -rc.c, 8388608.0f), t1 = fmaf(x1, -rc.c, 8388608.0f);
-          int32_t b0 = (int32_t)fbits(t0), b1 = (int32_t)fbits(t1);
-          b0 = min(max(b0, 0x4B000000), 0x4B000000 + L);
-          b1 = min(max(b1, 0x4B000000), 0x4B000000 + L);
+          // the clamp of l to [0, K] as one v_med3_f32 on t (floats on [2^23, 2^23 + K] order as
+          // their bit patterns)
+          const int32_t b0 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t0, 8388608.0f, kt_hi));
+          const int32_t b1 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t1, 8388608.0f, kt_hi));
           float w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
           float w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
           const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;

@@ -98,17 +98,19 @@ template <> struct Weight<WK_POTR> : PotW<false> {};
 template <> struct Weight<WK_POTR_FLUSH> : PotW<true> {};
 
 // K-interval, hard rounding.  t = y + 2^23 rounds y to the nearest integer
-// (ties to even) inside the float: bits(t) = 0x4B000000 + l.  The clip l <= K
-// is an integer min; (bits(t) << SH) drops the 0x4B000000 part (SH >= 8) and
-// leaves l * ROWS * 4, the table offset of entry l.
+// (ties to even) inside the float: bits(t) = 0x4B000000 + l.  The clip of l to
+// [0, K] is one v_med3_f32 on t (on [2^23, 2^23 + K] floats order as their bit
+// patterns; the lower end keeps the lookup in the table when rounding puts the
+// score a little above the anchor); (bits(t) << SH) drops the 0x4B000000 part
+// (SH >= 8) and leaves l * ROWS * 4, the table offset of entry l.
 template <bool FLUSH> struct KHardW {
+  static __device__ __forceinline__ int32_t level_bits(float y, int K) {
+    return (int32_t)fbits(__builtin_amdgcn_fmed3f(y + 8388608.0f, 8388608.0f, 8388608.0f + (float)K));
+  }
   template <int SH>
   static __device__ __forceinline__ float w(float acc, const RowC& r, const unsigned char* tab, int K) {
     const float y = fmaf(acc, -r.c, r.mc);
-    int32_t tb = (int32_t)fbits(y + 8388608.0f);
-    const int32_t hi = 0x4B000000 + K;
-    tb = tb < hi ? tb : hi;
-    tb = tb > 0x4B000000 ? tb : 0x4B000000;   // y >= 0 up to rounding; keeps the lookup in the table
+    const int32_t tb = level_bits(y, K);
     const float wv = *(const float*)(tab + (((uint32_t)tb << SH) + r.tab));
     if (FLUSH && y > (float)K) return 0.0f;
     return wv;
@@ -116,11 +118,7 @@ template <bool FLUSH> struct KHardW {
   static __device__ __forceinline__ uint32_t idx(float acc, const RowC& r, int K) {
     const float y = fmaf(acc, -r.c, r.mc);
     if (FLUSH && y > (float)K) return 254u;
-    int32_t tb = (int32_t)fbits(y + 8388608.0f);
-    const int32_t hi = 0x4B000000 + K;
-    tb = tb < hi ? tb : hi;
-    tb = tb > 0x4B000000 ? tb : 0x4B000000;
-    return (uint32_t)(tb - 0x4B000000);
+    return (uint32_t)(level_bits(y, K) - 0x4B000000);
   }
 };
 template <> struct Weight<WK_KH> : KHardW<false> {};
