@@ -267,8 +267,9 @@ __global__ __launch_bounds__(256, (keys_waves<D, WK>())) void bwd_keys(BwdArgs a
           const float* pk = Rp + r * NPARK;
           const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
           const float il = pk[2];
-          const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, il, pk[3], pk[4], pk[5],
-                                      __builtin_bit_cast(int, pk[6]), __builtin_bit_cast(int, pk[7]), Rg[r], minmax);
+          const float ds = dscore<WK>(a.mode, s, w, dp, key == __builtin_bit_cast(int, pk[6]),
+                                      key == __builtin_bit_cast(int, pk[7]), rc, Tb, f, il, pk[3], pk[4], pk[5], Rg[r],
+                                      minmax);
           qaxpy<D>(w * il, Gs + r * D, dv, u);
           qaxpy<D>(ds, Qs + r * D, dk, u);
         }
@@ -343,8 +344,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdArgs a) {
       const float dp = qdot<D>(Vs + j * D, g, u);
       if (key <= lim) {
         const float w = Weight<WK>::template w<SHB>(s, rc, Tb, f.levels);
-        const float ds = dscore<WK>(a.mode, s, w, dp, key, rc, Tb, f, il, pk[3], pk[4], pk[5], amax, amin, gd,
-                                    minmax);
+        const float ds = dscore<WK>(a.mode, s, w, dp, key == amax, key == amin, rc, Tb, f, il, pk[3], pk[4], pk[5],
+                                    gd, minmax);
         qaxpy<D>(ds, Ks + j * D, dq, u);
       }
     }

@@ -4,6 +4,8 @@
 // (BwdArgs::mode) are described in qsa_bwd.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "qsa_common.h"
 #include "qsa_weights.h"
 
@@ -28,6 +30,7 @@ struct GridD {
 // reciprocal and 1/K (K-interval).  STE: the rounding of the grid coordinate is passed straight through
 // where the clip to the last level is not active.  At y = K the last interval's slope applies,
 // and on a min-max grid every visible key is inside (its arg-min sits on y = K up to rounding).
+// w must be Weight<WK>::w of the same acc: hard rounding reads T_l off it (w = T_l there).
 template <int WK, int SHT = SHB>
 __device__ __forceinline__ void partials(float acc, float w, const RowC& rc, const unsigned char* Tb, int K,
                                          const GridD& gd, bool minmax, bool ste, float& gs, float& cm, float& clo) {
@@ -65,13 +68,21 @@ __device__ __forceinline__ void partials(float acc, float w, const RowC& rc, con
       dwdD = -Kf * e.x;
     }
   } else {
+    // Hard rounding: w = T_l = exp(-l Delta), l = min(rint(max(y, 0)), K), the level the weight
+    // was read at (outside a flushed window, where w = 0 and nothing moves).  Straight through,
+    // dw/dy = -Delta w, so the direct term -dw/dy / Delta is w itself; at fixed y dw/dDelta =
+    // -l w, and with y = (m - s) / Delta moving as well the total is w y - l w.  Written out
+    // here rather than through the general form below, which would multiply by Delta and by its
+    // reciprocal.
     const float r = __builtin_rintf(fmaxf(y, 0.0f));
     if (!(FLUSH && y > Kf)) {
-      const float lf = fminf(r, Kf);
-      const float tl = *(const float*)(Tb + ((((uint32_t)(int32_t)lf) << SHT) + rc.tab));
-      dwdD = -lf * tl;
-      if (ste && r <= Kf) dwdy = -gd.dsc * w;  // T_l = exp(-l Delta) with l := y
+      const float wo = (ste && r <= Kf) ? w : 0.0f;
+      const float dD = fmaf(wo, y, -fminf(r, Kf) * w);
+      gs = wo;
+      cm = minmax ? fmaf(dD, gd.ik, -wo) : -wo;
+      clo = minmax ? -dD * gd.ik : 0.0f;
     }
+    return;
   }
   const float inv = gd.idsc;
   gs = -dwdy * inv;
@@ -92,21 +103,60 @@ __device__ __forceinline__ GridD grid_d(const FwdArgs& f, float M, float MN) {
   return g;
 }
 
-// dS_ij from the weight, the row constants and dP_ij (modes as in the file header)
+// dS_ij from the weight, the row constants and dP_ij (modes as in the file header).  at_max and
+// at_min: key j is the row's arg-max (arg-min), where the attached modes add the gradient of m
+// (of lo on a min-max grid).
 template <int WK, int SHT = SHB>
-__device__ __forceinline__ float dscore(int mode, float s, float w, float dp, int key, const RowC& rc,
-                                        const unsigned char* Tb, const FwdArgs& f, float il, float Dr, float dm,
-                                        float dlo, int amax, int amin, const GridD& gd, bool minmax) {
+__device__ __forceinline__ float dscore(int mode, float s, float w, float dp, bool at_max, bool at_min,
+                                        const RowC& rc, const unsigned char* Tb, const FwdArgs& f, float il,
+                                        float Dr, float dm, float dlo, const GridD& gd, bool minmax) {
   if (mode == G_STE_POST) return (w * il) * (dp - Dr);  // il = 1 / l
   float gs, cm, clo;
   partials<WK, SHT>(s, w, rc, Tb, f.levels, gd, minmax, g_ste(mode), gs, cm, clo);
   float ds = (dp - Dr) * il * gs;
   if (g_attached(mode)) {
-    if (key == amax) ds += dm;
-    if (key == amin && minmax) ds += dlo;
+    if (at_max) ds += dm;
+    if (at_min && minmax) ds += dlo;
   }
   return ds;
 }
+
+// dscore with the gradient mode fixed at compile time (the matrix-core kernels instantiate their
+// element loops per mode, so that no per-element branch on the mode remains)
+template <int WK, int SHT, int MODE>
+__device__ __forceinline__ float dscore_m(float s, float w, float dp, bool at_max, bool at_min, const RowC& rc,
+                                          const unsigned char* Tb, const FwdArgs& f, float il, float Dr, float dm,
+                                          float dlo, const GridD& gd, bool minmax) {
+  if constexpr (MODE == G_STE_POST) {
+    return (w * il) * (dp - Dr);
+  } else {
+    constexpr bool STE = MODE == G_STE_PRE || MODE == G_STE_PRE_DET;
+    constexpr bool ATT = MODE == G_EXACT || MODE == G_STE_PRE;
+    float gs, cm, clo;
+    partials<WK, SHT>(s, w, rc, Tb, f.levels, gd, minmax, STE, gs, cm, clo);
+    float ds = (dp - Dr) * il * gs;
+    if constexpr (ATT) {
+      ds += at_max ? dm : 0.0f;
+      ds += (at_min && minmax) ? dlo : 0.0f;
+    }
+    return ds;
+  }
+}
+
+// Calls f(std::integral_constant<int, mode>) for the runtime gradient mode.
+template <class F>
+__device__ __forceinline__ void with_mode(int mode, F&& f) {
+  switch (mode) {
+    case G_STE_POST: f(std::integral_constant<int, G_STE_POST>()); break;
+    case G_EXACT: f(std::integral_constant<int, G_EXACT>()); break;
+    case G_EXACT_DET: f(std::integral_constant<int, G_EXACT_DET>()); break;
+    case G_STE_PRE: f(std::integral_constant<int, G_STE_PRE>()); break;
+    default: f(std::integral_constant<int, G_STE_PRE_DET>()); break;
+  }
+}
+
+// Offset of accumulator register r's key from the lane's first key (acc_key(r, hh) - 4 hh).
+__device__ __forceinline__ constexpr int acc_off(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // Block index -> (batch * KV head, key tile) for bwd_keys, on the same principles as the
 // query-tile map of the forward: each XCD (workgroup w runs on XCD w % 8) takes a contiguous

@@ -151,27 +151,51 @@ __global__ __launch_bounds__(MNW * 64, 2) void bwd_rows_m(BwdArgs a) {
     __syncthreads();
   };
 
+  // tiles t < tfull are visible to every row of the wave (rows past N are never read back)
+  const int tfull = ((f.causal ? min(wr0, N - 1) : N - 1) + 1) / MBN;
+  const bool minmax = wk_kint(WK) && !f.window_calib;
+  // the attached modes add the gradients of m and lo at the arg-max and arg-min: where those
+  // are nonzero (see calib below) pass 1 tracks the first key of each extremum
+  const bool calib = g_attached(a.mode) &&
+                     (WK == WK_TRUNC || wk_kint(WK) || ((WK == WK_POT || WK == WK_POT_FLUSH) && g_ste(a.mode)));
+  const bool need_min = minmax || calib;
+
   // pass 1: extrema over the visible keys, and the first keys that reach them
   float M = -__builtin_inff(), MN = __builtin_inff();
   int amax = 0x7FFFFFFF, amin = 0x7FFFFFFF;
+  auto extrema = [&](const f32x16& s, int k0, auto MASK, auto TRACK) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(MASK)::value, track = decltype(TRACK)::value;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + acc_off(r);  // increasing in r: the first key wins a tie
+      const bool ok = !masked || key <= lim;
+      if (track) {
+        const bool gt = ok && s[r] > M, lt = ok && s[r] < MN;
+        M = gt ? s[r] : M;
+        amax = gt ? key : amax;
+        MN = lt ? s[r] : MN;
+        amin = lt ? key : amin;
+      } else {
+        M = fmaxf(M, ok ? s[r] : -__builtin_inff());
+        if (need_min) MN = fminf(MN, ok ? s[r] : __builtin_inff());
+      }
+    }
+  };
+  auto pass1_tile = [&](int t, auto MASK) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16 s = prod(lds + (t & 1) * L::TT, kb, qf);
+      const int k0 = t * MBN + kb * 32 + 4 * hh;
+      if (calib) extrema(s, k0, MASK, std::true_type());
+      else extrema(s, k0, MASK, std::false_type());
+    }
+  };
   io.load(Kg, 0, N, lds, wave);
   done();
   for (int t = 0; t < T; ++t) {
     if (t + 1 < T) io.load(Kg, (t + 1) * MBN, N, lds + ((t + 1) & 1) * L::TT, wave);
-    if (t <= wlast) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x16 s = prod(lds + (t & 1) * L::TT, kb, qf);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * MBN + kb * 32 + acc_key(r, hh);  // increasing in r: the first key wins a tie
-          if (key <= lim) {
-            if (s[r] > M) { M = s[r]; amax = key; }
-            if (s[r] < MN) { MN = s[r]; amin = key; }
-          }
-        }
-      }
-    }
+    if (t < tfull) pass1_tile(t, std::false_type());
+    else if (t <= wlast) pass1_tile(t, std::true_type());
     done();
   }
   {  // the two half-waves of a row: larger (smaller) value, then the smaller key
@@ -187,13 +211,40 @@ __global__ __launch_bounds__(MNW * 64, 2) void bwd_rows_m(BwdArgs a) {
   if (row >= N) M = MN = 0.0f;
   const RowC rc = make_row<WK, MSH>(f, M, MN, wave * 32 + li, Tb, hh, 2);
   const GridD gd = grid_d(f, M, MN);
-  const bool minmax = wk_kint(WK) && !f.window_calib;
 
   // pass 2: l, D = sum_j P_ij dP_ij and (attached modes) the gradients of m and lo, which are
   // linear in D: sum dP cm and sum cm (likewise for lo) are gathered before D is known
-  const bool calib = g_attached(a.mode) &&
-                     (WK == WK_TRUNC || wk_kint(WK) || ((WK == WK_POT || WK == WK_POT_FLUSH) && g_ste(a.mode)));
   float l = 0.0f, wdp = 0.0f, pm = 0.0f, sm = 0.0f, plo = 0.0f, slo = 0.0f;
+  const bool ste = g_ste(a.mode);
+  auto sums = [&](const f32x16& s, const f32x16& dp, int k0, auto MASK, auto CALIB) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(MASK)::value, cal = decltype(CALIB)::value;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (!masked || k0 + acc_off(r) <= lim) {
+        const float w = Weight<WK>::template w<MSH>(s[r], rc, Tb, f.levels);
+        l += w;
+        wdp = fmaf(w, dp[r], wdp);
+        if (cal) {
+          float gs, cm, clo;
+          partials<WK, MSH>(s[r], w, rc, Tb, f.levels, gd, minmax, ste, gs, cm, clo);
+          pm = fmaf(dp[r], cm, pm);
+          sm += cm;
+          plo = fmaf(dp[r], clo, plo);
+          slo += clo;
+        }
+      }
+    }
+  };
+  auto pass2_tile = [&](int t, auto MASK) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16 s = prod(lds + (t & 1) * L::TT, kb, qf);
+      const f32x16 dp = prod(lds + (2 + (t & 1)) * L::TT, kb, gf);
+      const int k0 = t * MBN + kb * 32 + 4 * hh;
+      if (calib) sums(s, dp, k0, MASK, std::true_type());
+      else sums(s, dp, k0, MASK, std::false_type());
+    }
+  };
   io.load(Kg, 0, N, lds, wave);
   io.load(Vg, 0, N, lds + 2 * L::TT, wave);
   done();  // also publishes the K-interval tables
@@ -202,30 +253,8 @@ __global__ __launch_bounds__(MNW * 64, 2) void bwd_rows_m(BwdArgs a) {
       io.load(Kg, (t + 1) * MBN, N, lds + ((t + 1) & 1) * L::TT, wave);
       io.load(Vg, (t + 1) * MBN, N, lds + (2 + ((t + 1) & 1)) * L::TT, wave);
     }
-    if (t <= wlast) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x16 s = prod(lds + (t & 1) * L::TT, kb, qf);
-        const f32x16 dp = prod(lds + (2 + (t & 1)) * L::TT, kb, gf);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * MBN + kb * 32 + acc_key(r, hh);
-          if (key <= lim) {
-            const float w = Weight<WK>::template w<MSH>(s[r], rc, Tb, f.levels);
-            l += w;
-            wdp = fmaf(w, dp[r], wdp);
-            if (calib) {
-              float gs, cm, clo;
-              partials<WK, MSH>(s[r], w, rc, Tb, f.levels, gd, minmax, g_ste(a.mode), gs, cm, clo);
-              pm = fmaf(dp[r], cm, pm);
-              sm += cm;
-              plo = fmaf(dp[r], clo, plo);
-              slo += clo;
-            }
-          }
-        }
-      }
-    }
+    if (t < tfull) pass2_tile(t, std::false_type());
+    else if (t <= wlast) pass2_tile(t, std::true_type());
     done();
   }
   l = half_sum(l);
@@ -299,6 +328,41 @@ __global__ __launch_bounds__(MNW * 64, 2) void bwd_dq_m(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = zero16;
 
+  // tiles t < tfull are visible to every row of the wave (rows past N are never stored)
+  const int tfull = ((f.causal ? min(wr0, N - 1) : N - 1) + 1) / MBN;
+  // dS^T of the 32 keys of block kb, bf16, as the B operand of dQ^T += K^T dS^T (the score
+  // accumulator's layout: lane (i, h) holds 16 keys of query row i, packed by pairs)
+  auto block = [&](const lds_u8* Kt, int t, int kb, auto MASK, auto MODE) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(MASK)::value;
+    constexpr int mode = decltype(MODE)::value;
+    const f32x16 s = prod(Kt, kb, qf);
+    const f32x16 dp = prod(lds + (2 + (t & 1)) * L::TT, kb, gf);
+    const int k0 = t * MBN + kb * 32 + 4 * hh;
+    const int dmax = amax - k0, dmin = amin - k0;  // the extrema's offsets from the lane's first key
+    u32x4 dsb[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * kc + 2 * p + e;
+          float ds = 0.0f;
+          if (!masked || k0 + acc_off(r) <= lim) {
+            const float w = Weight<WK>::template w<MSH>(s[r], rc, Tb, f.levels);
+            ds = dscore_m<WK, MSH, mode>(s[r], w, dp[r], dmax == acc_off(r), dmin == acc_off(r), rc, Tb, f, il, pk[3],
+                                         pk[4], pk[5], gd, minmax);
+          }
+          ds2[e] = ds;
+        }
+        dsb[kc][p] = pack_bf16(ds2[0], ds2[1]);
+      }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq[db] = mma(io.cols(Kt, 2 * kb + kc, db), dsb[kc], dq[db]);
+  };
   io.load(Kg, 0, N, lds, wave);
   io.load(Vg, 0, N, lds + 2 * L::TT, wave);
   done();  // also publishes the K-interval tables
@@ -309,37 +373,13 @@ __global__ __launch_bounds__(MNW * 64, 2) void bwd_dq_m(BwdArgs a) {
     }
     if (t <= wlast) {
       const lds_u8* Kt = lds + (t & 1) * L::TT;
+      with_mode(a.mode, [&](auto MODE) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x16 s = prod(Kt, kb, qf);
-        const f32x16 dp = prod(lds + (2 + (t & 1)) * L::TT, kb, gf);
-        // dS^T of the 32 keys of block kb, bf16, as the B operand of dQ^T += K^T dS^T (the score
-        // accumulator's layout: lane (i, h) holds 16 keys of query row i, packed by pairs)
-        u32x4 dsb[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            float ds2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 8 * kc + 2 * p + e;
-              const int key = t * MBN + kb * 32 + acc_key(r, hh);
-              float ds = 0.0f;
-              if (key <= lim) {
-                const float w = Weight<WK>::template w<MSH>(s[r], rc, Tb, f.levels);
-                ds = dscore<WK, MSH>(a.mode, s[r], w, dp[r], key, rc, Tb, f, il, pk[3], pk[4], pk[5], amax, amin, gd,
-                                     minmax);
-              }
-              ds2[e] = ds;
-            }
-            dsb[kc][p] = pack_bf16(ds2[0], ds2[1]);
-          }
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) dq[db] = mma(io.cols(Kt, 2 * kb + kc, db), dsb[kc], dq[db]);
-      }
+        for (int kb = 0; kb < 2; ++kb) {
+          if (t < tfull) block(Kt, t, kb, std::false_type(), MODE);
+          else block(Kt, t, kb, std::true_type(), MODE);
+        }
+      });
     }
     done();
   }
@@ -429,8 +469,12 @@ __global__ __launch_bounds__(MNW * 64, 1) void bwd_keys_m(BwdArgs a) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      // P and dS of row block rb (32 query rows, a lane per row) for the wave's 32 keys, to the
+      // scratch as [row][key] bf16: keys 8j + 4h .. +3 (registers 4j .. 4j+3) are one 8-byte
+      // write per matrix
+      auto row_block = [&](int rb, auto MASK, auto MODE) __attribute__((always_inline)) {
+        constexpr bool masked = decltype(MASK)::value;
+        constexpr int mode = decltype(MODE)::value;
         const int rl = 32 * rb + li, row = r0 + rl;
         const f32x4 c0 = *(const f32x4*)(Pk + rl * NPARK), c1 = *(const f32x4*)(Pk + rl * NPARK + 4);
         const RowC rc = make_row<WK, SHB>(f, c0[0], c0[1], rl, nullptr, 0, 1);
@@ -439,28 +483,27 @@ __global__ __launch_bounds__(MNW * 64, 1) void bwd_keys_m(BwdArgs a) {
         // the arg-max and arg-min as scalars first: a bit cast of a vector element read the
         // vector's first element instead
         const float famax = c1[2], famin = c1[3];
-        const int amax = __builtin_bit_cast(int, famax), amin = __builtin_bit_cast(int, famin);
+        const int k0 = wk0 + 4 * hh;  // the lane's first key
+        const int dmax = __builtin_bit_cast(int, famax) - k0, dmin = __builtin_bit_cast(int, famin) - k0;
         f32x16 s = zero16, dp = zero16;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           s = mma(kf[c], io.rows(Qt, rb, c), s);
           dp = mma(vf[c], io.rows(Gt, rb, c), dp);
         }
-        // P and dS of the lane's row for the wave's 32 keys, to the scratch as [row][key] bf16:
-        // keys 8j + 4h .. +3 (registers 4j .. 4j+3) are one 8-byte write per matrix
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float pv[4], dv4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
-            const int key = wk0 + acc_key(r, hh);
+            const int key = k0 + acc_off(r);
             float p = 0.0f, ds = 0.0f;
-            if (row < N && key < N && (!f.causal || key <= row)) {
+            if (!masked || (row < N && key < N && (!f.causal || key <= row))) {
               const float w = Weight<WK>::template w<SHB>(s[r], rc, Tb, f.levels);
               p = w * il;
-              ds = dscore<WK, SHB>(a.mode, s[r], w, dp[r], key, rc, Tb, f, il, c0[3], c1[0], c1[1], amax, amin, gd,
-                                   minmax);
+              ds = dscore_m<WK, SHB, mode>(s[r], w, dp[r], dmax == acc_off(r), dmin == acc_off(r), rc, Tb, f, il,
+                                           c0[3], c1[0], c1[1], gd, minmax);
             }
             pv[e] = p;
             dv4[e] = ds;
@@ -470,7 +513,18 @@ __global__ __launch_bounds__(MNW * 64, 1) void bwd_keys_m(BwdArgs a) {
           *(__attribute__((address_space(3))) u32x2*)(Dw + o) =
               u32x2{pack_bf16(dv4[0], dv4[1]), pack_bf16(dv4[2], dv4[3])};
         }
-      }
+      };
+      with_mode(a.mode, [&](auto MODE) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          // every (row, key) of the block visible: its rows and the wave's keys inside the head,
+          // and (causal) the wave's last key at or before the block's first row
+          const int rf = r0 + 32 * rb;
+          const bool full = rf + 31 < N && wk0 + 31 < N && (!f.causal || wk0 + 31 <= rf);
+          if (full) row_block(rb, std::false_type(), MODE);
+          else row_block(rb, std::true_type(), MODE);
+        }
+      });
       // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows (four k-steps of 16 rows);
       // the scratch is this wave's own, written above in program order
 #pragma unroll
