@@ -112,6 +112,37 @@ def time_calls(fn, n, warmup=5):
     return t, float(np.median(host))
 
 
+def time_calls_interleaved(fns, n, rounds=5, warmup=3):
+    """time_calls for several kinds at once, taken in `rounds` interleaved rounds of n / rounds
+    calls per kind, so that a drift of the clock over the run (thermal, power) falls on every
+    kind alike: {name: (per-call ms, host call latency ms)}."""
+    for fn in fns.values():
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    per = max(1, n // rounds)
+    evs = {k: [] for k in fns}
+    for _ in range(rounds):
+        for k, fn in fns.items():
+            for _ in range(per):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                evs[k].append((a, b))
+        torch.cuda.synchronize()
+    out = {}
+    for k, fn in fns.items():
+        host = []
+        for _ in range(min(per * rounds, 10)):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            host.append((time.perf_counter() - t0) * 1e3)
+        out[k] = (np.array([a.elapsed_time(b) for a, b in evs[k]]), float(np.median(host)))
+    return out
+
+
 def host_cpu():
     """The host the oracle ran on: logical CPUs visible to this process and the CPU model."""
     model = None
@@ -495,17 +526,21 @@ def main(argv=None):
 
     if not args.no_variants:
         table = {}
-        for vname, vv in [("exact_online", {"kind": "exact"}), ("exact_anchored", {"kind": "exact_anchored"}),
-                          ("pot16", {"kind": "pot", "levels": 16}), ("pot8", {"kind": "pot", "levels": 8}),
-                          ("pot16_single_pass", {"kind": "pot_running", "levels": 16}),
-                          ("kint16_window8_hard", {"kind": "kint", "levels": 16, "window": 8.0}),
-                          ("kint16_minmax_hard", {"kind": "kint", "levels": 16}),
-                          ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True}),
-                          ("trunc_window2", {"kind": "trunc", "window": 2.0}),
-                          ("uniform_window2", {"kind": "uniform", "window": 2.0})]:
-            for c in (False, True):
-                t, host = time_calls(lambda: call(dev_t, x, vv, c, out), args.variant_calls)
-                Pc = pairs(B, H, N, c)
+        kinds = [("exact_online", {"kind": "exact"}), ("exact_anchored", {"kind": "exact_anchored"}),
+                 ("pot16", {"kind": "pot", "levels": 16}), ("pot8", {"kind": "pot", "levels": 8}),
+                 ("pot16_single_pass", {"kind": "pot_running", "levels": 16}),
+                 ("kint16_window8_hard", {"kind": "kint", "levels": 16, "window": 8.0}),
+                 ("kint16_minmax_hard", {"kind": "kint", "levels": 16}),
+                 ("kint16_window8_interp", {"kind": "kint", "levels": 16, "window": 8.0, "interp": True}),
+                 ("trunc_window2", {"kind": "trunc", "window": 2.0}),
+                 ("uniform_window2", {"kind": "uniform", "window": 2.0})]
+        for c in (False, True):
+            print(f"[bench] variants {'causal' if c else 'noncausal'}", file=sys.stderr, flush=True)
+            res = time_calls_interleaved({vname: (lambda vv=vv: call(dev_t, x, vv, c, out)) for vname, vv in kinds},
+                                         args.variant_calls)
+            Pc = pairs(B, H, N, c)
+            for vname, _ in kinds:
+                t, host = res[vname]
                 med = float(np.median(t))
                 table[f"{vname}:{'causal' if c else 'noncausal'}"] = {
                     "median_ms": round(med, 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
@@ -555,9 +590,11 @@ def bf16_block(wl, calls):
     table = {}
     for c in (False, True):
         Pc = pairs(B, H, N, c)
+        print(f"[bench] bf16 kinds {'causal' if c else 'noncausal'}", file=sys.stderr, flush=True)
+        res = time_calls_interleaved({vname: (lambda vv=vv: call(dev_b, xb, vv, c, ob)) for vname, vv in BF16_KINDS},
+                                     calls)
         for vname, vv in BF16_KINDS:
-            print(f"[bench] bf16 {vname} {'causal' if c else 'noncausal'}", file=sys.stderr, flush=True)
-            t, host = time_calls(lambda: call(dev_b, xb, vv, c, ob), calls)
+            t, host = res[vname]
             med = float(np.median(t))
             tf = 4 * d * Pc / (med * 1e-3) / 1e12
             table[f"{vname}:{'causal' if c else 'noncausal'}"] = {
@@ -567,7 +604,7 @@ def bf16_block(wl, calls):
                 "mfma_frac": round(mfma_flops_per_pair(vv["kind"], d) * Pc / (med * 1e-3) / 1e12 /
                                    PEAK_TFLOPS["bf16"], 4)}
     out = {"config": {"B": B, "H": H, "Hkv": xb.k.shape[1], "N": N, "d": d, "dtype": "bf16"},
-           "calls": calls, "variants": table}
+           "calls": calls, "timing": "kinds interleaved in 5 rounds per causality", "variants": table}
     for c in ("noncausal", "causal"):
         p, e = table[f"pot16:{c}"], table[f"exact_anchored:{c}"]
         out.setdefault("pot_vs_exact_anchored", {})[c] = {"speedup": round(e["median_ms"] / p["median_ms"], 4),
