@@ -74,10 +74,14 @@ __device__ __forceinline__ void partials(float acc, float w, const RowC& rc, con
     // -l w, and with y = (m - s) / Delta moving as well the total is w y - l w.  Written out
     // here rather than through the general form below, which would multiply by Delta and by its
     // reciprocal.
-    const float r = __builtin_rintf(fmaxf(y, 0.0f));
+    // As in the weight (KHardW): t = y + 2^23 holds rint(y) in its low bits and the clamp of
+    // t to [2^23, 2^23 + K] gives l = min(rint(max(y, 0)), K); rint(y) <= K exactly when
+    // t <= 2^23 + K.  Written the same way, the compiler shares t and the clamp with the weight.
+    const float t = y + 8388608.0f;
     if (!(FLUSH && y > Kf)) {
-      const float wo = (ste && r <= Kf) ? w : 0.0f;
-      const float dD = fmaf(wo, y, -fminf(r, Kf) * w);
+      const float lf = __builtin_amdgcn_fmed3f(t, 8388608.0f, 8388608.0f + Kf) - 8388608.0f;
+      const float wo = (ste && t <= 8388608.0f + Kf) ? w : 0.0f;
+      const float dD = fmaf(wo, y, -lf * w);
       gs = wo;
       cm = minmax ? fmaf(dD, gd.ik, -wo) : -wo;
       clo = minmax ? -dD * gd.ik : 0.0f;
@@ -134,12 +138,13 @@ __device__ __forceinline__ float dscore_m(float s, float w, float dp, bool at_ma
     constexpr bool ATT = MODE == G_EXACT || MODE == G_STE_PRE;
     float gs, cm, clo;
     partials<WK, SHT>(s, w, rc, Tb, f.levels, gd, minmax, STE, gs, cm, clo);
-    float ds = (dp - Dr) * il * gs;
+    const float g = fmaf(dp, il, -Dr * il);  // (dP - D) / l; D il is the same for the whole row
     if constexpr (ATT) {
-      ds += at_max ? dm : 0.0f;
-      ds += (at_min && minmax) ? dlo : 0.0f;
+      const float ext = (at_max ? dm : 0.0f) + ((at_min && minmax) ? dlo : 0.0f);
+      return fmaf(g, gs, ext);
+    } else {
+      return g * gs;
     }
-    return ds;
   }
 }
 
