@@ -1,7 +1,8 @@
 // Fused quantized-softmax attention forward, OCP fp8 e4m3 Q/K/V with
 // per-tensor descales (O in bf16), gfx950 MFMA.
 //
-// Same structure as the bf16 kernel (one workgroup = 4 waves = 128 query rows;
+// Same structure as the bf16 kernel (one workgroup = 4 waves = 128 query rows, 8 waves = 256
+// rows for PoT at d = 128;
 // S^T = K Q^T so a lane owns a query row; true-row-max pre-pass; main-loop
 // accumulators start at -M; LDS tiles filled ahead of use with one barrier per
 // tile; masking only on a wave's last tile), with the score product on the
@@ -38,9 +39,9 @@ namespace {
 #define QSA_FP8_POT_PV16 0
 #endif
 
-constexpr int NW = 4;    // waves per workgroup
+constexpr int NW = 4;    // waves per workgroup (8 for PoT at d = 128, see launch_one)
 constexpr int BN = 64;   // keys per tile
-constexpr int BM = 128;  // query rows per workgroup
+constexpr int BM = 128;  // query rows per workgroup (NW * 32)
 constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
 
 // Slot of 16-byte chunk c of fp8 V row r is c ^ vswz(r) (row bits 1 and 3 for d = 128, bit 3
@@ -70,8 +71,8 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 // 32 bits before its low 16 bits are used (the launcher proves when it cannot; PoT only).
 // Anchored kinds (all but the online exact control) run after rowext_fp8, which leaves each
 // row's score extrema parked in O; the kernel reads them back before it writes O.
-template <int D, int WK, bool DUMP, bool WIDE>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
+template <int D, int WK, bool DUMP, bool WIDE, int NWT = NW>
+__global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
@@ -88,9 +89,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   constexpr int KR = SK * 16, VR = SV * 16;
   auto vswz = [](int r) { return vswz_of<D>(r); };
   constexpr int KT = BN * KR, VT = BN * VR;
-  constexpr int KIW = SK / NW;  // K-tile load instructions per wave
-  static_assert(SK % NW == 0, "K tiles split evenly over the waves");
-  constexpr int VIW = (SV + NW - 1) / NW;
+  constexpr int KIW = SK / NWT;  // K-tile load instructions per wave
+  static_assert(SK % NWT == 0, "K tiles split evenly over the waves");
+  constexpr int VIW = (SV + NWT - 1) / NWT;
   // LDS tile buffers: PoT three each for K and V (its loop is described there); the other
   // kinds keep K two tiles ahead and a register-staged V one tile ahead (two buffers each),
   // which measures faster for them.
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int kvh = h / (a.H / a.Hkv);
   const int N = a.N;
-  const int q0 = qt * BM;
+  const int q0 = qt * (NWT * 32);
   const int wr0 = q0 + wave * 32;
   const int row = wr0 + li;
   const uint8_t* Qg = (const uint8_t*)a.q + (size_t)(b * a.H + h) * N * D;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     qf[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 
-  const int T = a.causal ? ((min(q0 + BM, N) - 1) / BN + 1) : (N + BN - 1) / BN;
+  const int T = a.causal ? ((min(q0 + (NWT * 32), N) - 1) / BN + 1) : (N + BN - 1) / BN;
   const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
   const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
 
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   uint32_t kvo[KIW];
 #pragma unroll
   for (int m = 0; m < KIW; ++m) {
-    const int sl = (wave + NW * m) * 64 + lane, j = sl / SK;
+    const int sl = (wave + NWT * m) * 64 + lane, j = sl / SK;
     kvo[m] = (uint32_t)(j * D + ((sl % SK) ^ kswz_of<D>(j)) * 16);
   }
   auto tile_rsrc = [&](const uint8_t* base, int kt) {
@@ -154,14 +155,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
 #pragma unroll
     for (int m = 0; m < KIW; ++m)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds + off + (wave + NW * m) * 1024), 16, kvo[m], 0, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(lds + off + (wave + NWT * m) * 1024), 16, kvo[m], 0, 0, 0);
   };
   auto load_k = [&](int kt, int buf) { load_k_at(kt, buf * KT); };
   uint32_t vvo[PV8 ? VIW : 1];
   if (PV8) {
 #pragma unroll
     for (int m = 0; m < VIW; ++m) {
-      const int sl = (wave + NW * m) * 64 + lane, j = sl / SV;
+      const int sl = (wave + NWT * m) * 64 + lane, j = sl / SV;
       vvo[m] = (uint32_t)(j * D + ((sl % SV) ^ vswz(j)) * 16);  // slot (j, c') holds chunk c' ^ vswz(j)
     }
   }
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
     if (PV8) {
 #pragma unroll
-      for (int m = 0; m < VIW; ++m)  // SV % NW == 0: every wave issues VIW of them
+      for (int m = 0; m < VIW; ++m)  // SV % NWT == 0: every wave issues VIW of them
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + VB0 + buf * VT + (wave + NW * m) * 1024), 16,
+            r, (__attribute__((address_space(3))) void*)(lds + VB0 + buf * VT + (wave + NWT * m) * 1024), 16,
             vvo[m], 0, 0, 0);
     } else {
 #pragma unroll
@@ -210,9 +211,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8(FwdArgs a) {
   };
   auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // Wait for this wave's LDS-direct loads except the newest N.  Tile loads are split over the
-  // waves (wave w issues slots w, w+NW, ...): SLOTS/NW of them, plus one when w < SLOTS % NW.
-  constexpr int NK_MIN = SK / NW, NV_MIN = PV8 ? SV / NW : 0;
-  static_assert(!PV8 || SV % NW == 0, "PoT V tiles split evenly over the waves");
+  // waves (wave w issues slots w, w+NWT, ...): SLOTS/NWT of them, plus one when w < SLOTS % NWT.
+  constexpr int NK_MIN = SK / NWT, NV_MIN = PV8 ? SV / NWT : 0;
+  static_assert(!PV8 || SV % NWT == 0, "PoT V tiles split evenly over the waves");
   auto loads_done_but = [&](auto n) {
     constexpr int N = DUMP ? 0 : decltype(n)::value;  // the index dump's stores also count in vmcnt
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -940,8 +941,15 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does (the single-pass
   // anchor adds less than 1 to y, inside the margin to 2^15)
   const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
-  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false>
-                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8> : (const void*)fwd_fp8<D, WK, false, false>;
+  // PoT with the 8-bit PV at d = 128: 8 waves (256 query rows) per workgroup and one
+  // workgroup per CU, the same 2 waves per SIMD; a K or V tile is then one load instruction
+  // per wave (measured 0.649 -> 0.643 ms at 8K non-causal, causal unchanged).  The other kinds
+  // stage V with one thread per quarter row of a 64-row tile, which needs 256 threads.
+  constexpr int NWK = (PV8 && !wk_running(WK) && D == 128) ? 8 : NW;
+  a.n_qtiles = (a.N + NWK * 32 - 1) / (NWK * 32);
+  a.total_blocks = a.B * a.H * a.n_qtiles;
+  const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false, NWK>
+                                : wide ? (const void*)fwd_fp8<D, WK, false, PV8, NWK> : (const void*)fwd_fp8<D, WK, false, false, NWK>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -959,11 +967,11 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, true, false, NWK>), dim3(a.total_blocks), dim3(NWK * 64), lds, st, a);
   else if (wide)
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, PV8, NWK>), dim3(a.total_blocks), dim3(NWK * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_fp8<D, WK, false, false, NWK>), dim3(a.total_blocks), dim3(NWK * 64), lds, st, a);
   return hipGetLastError();
 }
 
