@@ -78,8 +78,13 @@ template <int D> struct Lay {
   static_assert(SL % NW == 0, "tiles split evenly over the waves");
 };
 
+// Workgroups per CU the register budget is sized for: 3 at d = 64 (at most 168 VGPRs, which
+// the d = 64 kernels fit without spills), so that the short, latency-bound rows of small heads
+// have three waves per SIMD to interleave; 2 at d = 128 (the O accumulator alone is 64 VGPRs).
+template <int D> constexpr int fwd_occ() { return D == 64 ? 3 : 2; }
+
 template <int D, int WK, bool DUMP, bool TAB>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
