@@ -5,8 +5,9 @@
 // laid out for CDNA4:
 //
 //   * one workgroup = 4 waves = 128 query rows of one (batch, head), two
-//     workgroups per CU (two waves per SIMD); each wave owns 32 rows for the
-//     whole kernel (its Q^T operand stays in VGPRs);
+//     workgroups per CU (two waves per SIMD), or at d = 128 for most kinds
+//     8 waves = 256 rows, one workgroup per CU (see fwd_waves); each wave owns
+//     32 rows for the whole kernel (its Q^T operand stays in VGPRs);
 //   * scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: lane (i, h) of a wave holds query row i and 16
 //     keys of each 32-key block, so row maxima are in-lane reductions plus one
@@ -45,11 +46,11 @@
 namespace qsa {
 namespace {
 
-constexpr int NW = 4;   // waves per workgroup
+constexpr int NW = 4;   // waves per workgroup (8 for the kinds fwd_waves names)
 constexpr int BN = 64;  // keys per tile
 constexpr int NS = 2;   // K and V stages in LDS
 constexpr int KTAB_MAX = 16;  // largest K with a per-row grid table in LDS
-constexpr int BM = NW * 32;   // query rows per workgroup
+constexpr int BM = NW * 32;   // query rows per workgroup of NW waves
 constexpr int SH = 9;         // log2(BM * 4): the K-interval table's stride between grid values of one row
 
 // Slot of 16-byte chunk q of K row r is q ^ kswz(r): a ds_read_b128 of the score loop reads
@@ -82,14 +83,27 @@ template <int D> struct Lay {
 // the d = 64 kernels fit without spills), so that the short, latency-bound rows of small heads
 // have three waves per SIMD to interleave; 2 at d = 128 (the O accumulator alone is 64 VGPRs).
 template <int D> constexpr int fwd_occ() { return D == 64 ? 3 : 2; }
+// Waves per workgroup.  At d = 128 the exact, PoT, single-pass and interpolating kinds run 8
+// waves (256 query rows) and one workgroup per CU: the same two waves per SIMD, but each K or V
+// tile is half the load instructions per wave and one LDS copy serves twice the rows, and the
+// kernel fits in fewer registers (216-245 VGPRs against 245-256).  Measured at 8K against 4
+// waves: exact online 3.8 % / 2.4 % faster (non-causal / causal), single-pass PoT 3.3 % / 2.3 %,
+// PoT 1.4 % / 0.7 %, exact anchored 1.8 % / 0.4 %, interpolation 1.7 % / 0.5 %.  Hard rounding
+// and the support kinds measured 0.6-2.5 % slower with 8 and keep 4, as does d = 64, whose
+// register budget is sized for three 4-wave workgroups per CU instead (fwd_occ).
+template <int D, int WK> constexpr int fwd_waves() {
+  return (D == 128 && (WK == WK_EXACT || WK == WK_EXACT_ANCH || wk_pot(WK) || WK == WK_KI || WK == WK_KI_FLUSH)) ? 8
+                                                                                                                  : NW;
+}
 
-template <int D, int WK, bool DUMP, bool TAB>
-__global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
+template <int D, int WK, bool DUMP, bool TAB, int NWT = NW>
+__global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-column blocks of O^T
   using LY = Lay<D>;
-  constexpr int SL = LY::SL, RR = LY::RR, KT = LY::KT, VT = LY::VT, LW = LY::LW;
+  constexpr int SHK = NWT == 8 ? SH + 1 : SH;  // K-interval table stride shift for NWT * 32 rows
+  constexpr int SL = LY::SL, RR = LY::RR, KT = LY::KT, VT = LY::VT, LW = SL / NWT;
   constexpr bool RUN = wk_running(WK);             // single-pass PoT: running integer anchor
   constexpr bool ANCH = (WK != WK_EXACT) && !RUN;  // row extrema from the pre-pass
   constexpr bool EXACT_W = (WK == WK_EXACT || WK == WK_EXACT_ANCH);
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int kvh = h / (a.H / a.Hkv);
   const int N = a.N;
-  const int q0 = qt * BM;
+  const int q0 = qt * (NWT * 32);
   const int wr0 = q0 + wave * 32;
   const int row = wr0 + li;
   const int lim = a.causal ? min(row, N - 1) : N - 1;  // last key visible to this lane's row
@@ -126,27 +140,27 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
   for (int c = 0; c < KC; ++c)
     qf[c] = row < N ? *(const u32x4*)(Qg + (size_t)row * D + 16 * c + 8 * hh) : u32x4{0, 0, 0, 0};
 
-  const int T = a.causal ? ((min(q0 + BM, N) - 1) / BN + 1) : (N + BN - 1) / BN;  // tiles of this workgroup
+  const int T = a.causal ? ((min(q0 + (NWT * 32), N) - 1) / BN + 1) : (N + BN - 1) / BN;  // tiles of this workgroup
   // last tile this wave computes (-1: none); only that tile can need masking
   const int wlast = wr0 >= N ? -1 : (a.causal ? (min(wr0 + 31, N - 1) / BN) : T - 1);
   const bool last_masked = (a.causal && wlast * BN + BN - 1 > wr0) || (wlast * BN + BN > N);
   const int tclean = last_masked ? wlast : wlast + 1;  // tiles t < tclean need no mask
 
   // ---- tile staging: buffer loads straight into LDS ------------------------------------------
-  // Instruction m of a wave writes the 64 consecutive 16-byte slots (wave + NW m) * 64 + lane:
+  // Instruction m of a wave writes the 64 consecutive 16-byte slots (wave + NWT m) * 64 + lane:
   // slot s of a tile is row j = s / SL, position s % SL of the row, which holds chunk
   // (s % SL) ^ swz(j).  The per-tile buffer resource starts at the tile and ends at the end of
   // the head, so rows past N read as zero.
-  // Instruction m covers rows 64 NW m / SL further on than instruction 0 (a multiple of 16), the
+  // Instruction m covers rows 64 NWT m / SL further on than instruction 0 (a multiple of 16), the
   // same position in the row and the same swizzle (which reads row bits below 4): its global
-  // offset is instruction 0's plus m * 64 NW * 16 bytes, taken as the scalar offset.
+  // offset is instruction 0's plus m * 64 NWT * 16 bytes, taken as the scalar offset.
   uint32_t kvo, vvo;
   {
     const int sl = wave * 64 + lane, j = sl / SL, c = sl % SL;
     kvo = (uint32_t)(j * D + 8 * (c ^ kswz_of<D>(j))) * 2;
     vvo = (uint32_t)(j * D + 8 * (c ^ vswz_of<D>(j))) * 2;
   }
-  static_assert((NW * 64 / SL) % 16 == 0, "the swizzles repeat every 16 rows");
+  static_assert((NWT * 64 / SL) % 16 == 0, "the swizzles repeat every 16 rows");
   auto tile_rsrc = [&](const __bf16* base, int kt) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)kt * BN * D), 0, (N - kt * BN) * D * 2,
                                              0x00020000);
@@ -156,16 +170,16 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
 #pragma unroll
     for (int m = 0; m < LW; ++m)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds + st * KT + (wave + NW * m) * 1024), 16, kvo,
-          m * NW * 64 * 16, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(lds + st * KT + (wave + NWT * m) * 1024), 16, kvo,
+          m * NWT * 64 * 16, 0, 0);
   };
   auto load_v = [&](int kt, int st) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
 #pragma unroll
     for (int m = 0; m < LW; ++m)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds + LY::V0 + st * VT + (wave + NW * m) * 1024), 16, vvo,
-          m * NW * 64 * 16, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(lds + LY::V0 + st * VT + (wave + NWT * m) * 1024), 16, vvo,
+          m * NWT * 64 * 16, 0, 0);
   };
   auto loads_done = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
     M = row < N ? bitsf(park[0]) : 0.0f;
     MN = row < N ? bitsf(park[1]) : 0.0f;
   }
-  RowC rc = make_row<WK, SH, true>(a, M, MN, wave * 32 + li, TAB ? Tb : nullptr, hh, 2);
+  RowC rc = make_row<WK, SHK, true>(a, M, MN, wave * 32 + li, TAB ? Tb : nullptr, hh, 2);
   // interpolation: T_l+1 = T_l e^-Delta = T_l 2^step
   const float rstep = INTERP && TAB ? __builtin_amdgcn_exp2f(rc.step) - 1.0f : 0.0f;
   // main-loop score accumulators start at -M: s' = acc - M
@@ -361,9 +375,9 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
           const int32_t b0 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t0, 8388608.0f, kt_hi));
           const int32_t b1 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t1, 8388608.0f, kt_hi));
           float w0, w1;
-          if (TAB) {  // T_l from the row's column of the table: (bits << SH) drops 0x4B000000
-            w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
-            w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
+          if (TAB) {  // T_l from the row's column of the table: (bits << SHK) drops 0x4B000000
+            w0 = *(const float*)(Tb + (((uint32_t)b0 << SHK) + rc.tab));
+            w1 = *(const float*)(Tb + (((uint32_t)b1 << SHK) + rc.tab));
           } else {
             w0 = __builtin_amdgcn_exp2f(rc.step * (float)(b0 - 0x4B000000));
             w1 = __builtin_amdgcn_exp2f(rc.step * (float)(b1 - 0x4B000000));
@@ -385,8 +399,8 @@ __global__ __launch_bounds__(NW * 64, fwd_occ<D>()) void fwd_bf16(FwdArgs a) {
           const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
           float w0, w1;
           if (TAB) {  // T_l (1 + t (e^-Delta - 1)); at l = K the parameter t is 0
-            const float T0 = *(const float*)(Tb + ((l0 << SH) + rc.tab));
-            const float T1 = *(const float*)(Tb + ((l1 << SH) + rc.tab));
+            const float T0 = *(const float*)(Tb + ((l0 << SHK) + rc.tab));
+            const float T1 = *(const float*)(Tb + ((l1 << SHK) + rc.tab));
             w0 = T0 * fmaf(c0 - f0, rstep, 1.0f);
             w1 = T1 * fmaf(c1 - f1, rstep, 1.0f);
           } else {
@@ -733,17 +747,21 @@ __global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
 
 template <int D, int WK, bool TAB>
 hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
+  constexpr int NWK = fwd_waves<D, WK>();
   // the table holds T_l alone for both hard rounding and interpolation
-  const size_t lds = (size_t)Lay<D>::TAB + (TAB ? (size_t)BM * (a.levels + 1) * 4 : 0);
-  const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true, TAB> : (const void*)fwd_bf16<D, WK, false, TAB>;
+  const size_t lds = (size_t)Lay<D>::TAB + (TAB ? (size_t)(NWK * 32) * (a.levels + 1) * 4 : 0);
+  FwdArgs g = a;  // query tiles of NWK * 32 rows
+  g.n_qtiles = (a.N + NWK * 32 - 1) / (NWK * 32);
+  g.total_blocks = a.B * a.H * g.n_qtiles;
+  const void* kern = a.grid_idx ? (const void*)fwd_bf16<D, WK, true, TAB, NWK> : (const void*)fwd_bf16<D, WK, false, TAB, NWK>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   if (a.grid_idx)
-    hipLaunchKernelGGL((fwd_bf16<D, WK, true, TAB>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_bf16<D, WK, true, TAB, NWK>), dim3(g.total_blocks), dim3(NWK * 64), lds, st, g);
   else
-    hipLaunchKernelGGL((fwd_bf16<D, WK, false, TAB>), dim3(a.total_blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((fwd_bf16<D, WK, false, TAB, NWK>), dim3(g.total_blocks), dim3(NWK * 64), lds, st, g);
   return hipGetLastError();
 }
 
