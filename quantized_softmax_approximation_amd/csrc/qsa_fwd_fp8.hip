@@ -2,7 +2,7 @@
 // per-tensor descales (O in bf16), gfx950 MFMA.
 //
 // Same structure as the bf16 kernel (one workgroup = 4 waves = 128 query rows, 8 waves = 256
-// rows for PoT at d = 128;
+// rows at d = 128 for every kind but the single pass;
 // S^T = K Q^T so a lane owns a query row; true-row-max pre-pass; main-loop
 // accumulators start at -M; LDS tiles filled ahead of use with one barrier per
 // tile; masking only on a wave's last tile), with the score product on the
@@ -39,9 +39,9 @@ namespace {
 #define QSA_FP8_POT_PV16 0
 #endif
 
-constexpr int NW = 4;    // waves per workgroup (8 for PoT at d = 128, see launch_one)
+constexpr int NW = 4;    // waves per workgroup (8 at d = 128 for most kinds, see launch_one)
 constexpr int BN = 64;   // keys per tile
-constexpr int BM = 128;  // query rows per workgroup (NW * 32)
+constexpr int BM = 128;  // query rows per workgroup of NW waves
 constexpr int SH = 9;    // log2(BM * 4): K-interval table row stride shift
 
 // Slot of 16-byte chunk c of fp8 V row r is c ^ vswz(r) (row bits 1 and 3 for d = 128, bit 3
@@ -75,6 +75,7 @@ template <int D, int WK, bool DUMP, bool WIDE, int NWT = NW>
 __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass needs only the signature (for the launch stub)
   constexpr int KC = D / 64;  // k-steps of the QK product
+  constexpr int SHK = NWT == 8 ? SH + 1 : SH;  // K-interval table stride shift for NWT * 32 rows
   constexpr int DB = D / 32;  // 32-column blocks of O^T
   constexpr bool RUN = wk_running(WK);                // single-pass PoT: running integer anchor
   constexpr bool ANCH = (WK != WK_EXACT) && !RUN;     // read the pre-pass extrema
@@ -167,10 +168,10 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
     }
   }
   // bf16-PV kinds: each thread widens a quarter row of V (D/4 fp8 -> bf16) into LDS
-  constexpr int VQ = D / 4;        // bytes of V a thread stages
+  constexpr int VQ = D / NWT;      // bytes of V a thread stages (NWT threads per row)
   constexpr int VQL = VQ / 16;     // 16-byte loads per thread
   u32x4 vst[PV8 ? 1 : VQL];
-  const int vrow = tid >> 2, vpart = tid & 3;
+  const int vrow = tid / NWT, vpart = tid % NWT;
   auto load_v = [&](int kt, int buf) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vg, kt);
     if (PV8) {
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
     MN = row < N ? bitsf(park[1]) : 0.0f;
   }
 
-  RowC rc = make_row<WK, SH>(a, M, MN, wave * 32 + li, Tb, hh, 2);
+  RowC rc = make_row<WK, SHK>(a, M, MN, wave * 32 + li, Tb, hh, 2);
   f32x16 init16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
@@ -397,8 +398,8 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
           // their bit patterns)
           const int32_t b0 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t0, 8388608.0f, kt_hi));
           const int32_t b1 = (int32_t)fbits(__builtin_amdgcn_fmed3f(t1, 8388608.0f, kt_hi));
-          float w0 = *(const float*)(Tb + (((uint32_t)b0 << SH) + rc.tab));
-          float w1 = *(const float*)(Tb + (((uint32_t)b1 << SH) + rc.tab));
+          float w0 = *(const float*)(Tb + (((uint32_t)b0 << SHK) + rc.tab));
+          float w1 = *(const float*)(Tb + (((uint32_t)b1 << SHK) + rc.tab));
           const float y0 = FLUSH ? -x0 * rc.c : 0.0f, y1 = FLUSH ? -x1 * rc.c : 0.0f;
           if (FLUSH) {
             w0 = y0 > Kf ? 0.0f : w0;
@@ -415,8 +416,8 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
           const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
           const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
           typedef float f2 __attribute__((ext_vector_type(2)));
-          const f2 e0 = *(const f2*)(Tb + ((l0 << (SH + 1)) + rc.tab));
-          const f2 e1 = *(const f2*)(Tb + ((l1 << (SH + 1)) + rc.tab));
+          const f2 e0 = *(const f2*)(Tb + ((l0 << (SHK + 1)) + rc.tab));
+          const f2 e1 = *(const f2*)(Tb + ((l1 << (SHK + 1)) + rc.tab));
           float w0 = fmaf(c0 - f0, e0.y, e0.x), w1 = fmaf(c1 - f1, e1.y, e1.x);
           if (FLUSH) {
             w0 = y0 > Kf ? 0.0f : w0;
@@ -936,16 +937,17 @@ hipError_t launch_one(const FwdArgs& a0, hipStream_t st) {
   constexpr bool ANCH = WK != WK_EXACT && !wk_running(WK);
   constexpr int SK = D / 16, SV = PV8 ? D / 16 : (D / 8 + 4);
   constexpr int NB = PV8 ? 3 : 2;  // K and V tile buffers
-  const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, BM, a.levels);
+  // d = 128: 8 waves (256 query rows) per workgroup and one workgroup per CU, the same 2 waves
+  // per SIMD; a K or V tile is then half the load instructions per wave and one LDS copy serves
+  // twice the rows (the bf16-PV kinds stage V an eighth of a row per thread).  Measured at 8K
+  // against 4 waves: PoT 0.649 -> 0.643 ms non-causal; the bf16-PV kinds 5-13 % faster.  The
+  // single-pass kind measured 5-6 % slower with 8 and keeps 4.
+  constexpr int NWK = (D == 128 && !wk_running(WK)) ? 8 : NW;
+  const size_t lds = (size_t)BN * NB * (SK + SV) * 16 + table_bytes(WK, NWK * 32, a.levels);
   // PoT: |raw score| <= d * 448^2 for e4m3 inputs, so y = (m - s) * scale * log2 e stays below
   // 2^15 (no 16-bit wrap of the exponent) whenever 2 d 448^2 sc log2 e does (the single-pass
   // anchor adds less than 1 to y, inside the margin to 2^15)
   const bool wide = PV8 && 2.0 * D * 448.0 * 448.0 * (double)a.sc * 1.4426950408889634 >= 32000.0;
-  // PoT with the 8-bit PV at d = 128: 8 waves (256 query rows) per workgroup and one
-  // workgroup per CU, the same 2 waves per SIMD; a K or V tile is then one load instruction
-  // per wave (measured 0.649 -> 0.643 ms at 8K non-causal, causal unchanged).  The other kinds
-  // stage V with one thread per quarter row of a 64-row tile, which needs 256 threads.
-  constexpr int NWK = (PV8 && !wk_running(WK) && D == 128) ? 8 : NW;
   a.n_qtiles = (a.N + NWK * 32 - 1) / (NWK * 32);
   a.total_blocks = a.B * a.H * a.n_qtiles;
   const void* kern = a.grid_idx ? (const void*)fwd_fp8<D, WK, true, false, NWK>
