@@ -90,7 +90,7 @@ def test_gqa16k_sampled(gqa16k, var):
 
 # ---------------------------------------------------------------- ragged tails, tiny N, GQA, d
 
-EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 200, 333]
+EDGE_N = [1, 2, 17, 63, 64, 65, 127, 129, 200, 255, 257, 333]
 
 
 @pytest.mark.parametrize("N", EDGE_N)
@@ -276,7 +276,7 @@ def test_fp8_8k_sampled(fp8_8k, var, causal):
                   windows=gc.sample_windows(wl.N, n=3, seed=8), x=x, dev_t=dev_t, f64=f64)
 
 
-@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 333])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 255, 257, 333])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_ragged(N, d, causal):

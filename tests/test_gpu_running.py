@@ -70,7 +70,7 @@ def test_fp8_8k_sampled(fp8_8k, var, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 333])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 255, 257, 333])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged(dtype, N, causal):
     for d in (64, 128):
