@@ -36,8 +36,8 @@
  *   Pointers  Q, K, V, O and every optional output are DEVICE pointers owned
  *             by the caller.  The library allocates nothing, keeps no state
  *             between calls and needs no workspace.  O must not overlap Q, K
- *             or V: for fp8 inputs and the anchored kinds the call runs two
- *             kernels on `stream`, and the first parks the rows' score
+ *             or V: for bf16 and fp8 inputs and the anchored kinds the call
+ *             runs two kernels on `stream`, and the first parks the rows' score
  *             extrema in O (8 bytes per row, inside the rows of the same
  *             32-row block) for the second, which then overwrites them.
  *   Streams   `stream` is a hipStream_t passed as void* (NULL: the null
