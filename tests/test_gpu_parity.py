@@ -125,11 +125,13 @@ def test_bf16_8k_sampled(bf16_8k, var, causal):
                   windows=gc.sample_windows(wl.N, n=3, seed=12), x=x, dev_t=dev_t, f64=f64)
 
 
-@pytest.mark.parametrize("N", [1, 5, 64, 100])
-def test_ragged_fp32(N):
-    wl = qin.custom(f"f32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
+@pytest.mark.parametrize("N", [1, 5, 64, 100, 129, 200, 257])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_fp32(N, causal):
+    # fp32 kernel: 128-row workgroups, 64-key tiles; N = 129 and 257 start a new workgroup
+    wl = qin.custom(f"f32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=causal, sigma_qk=1.2, seed=N)
     x = qin.make_inputs(wl)
-    for var in (gc.EXACT, gc.POT8, gc.KH4, gc.KI4W, gc.TRUNC2, gc.UNIF2, gc.KH4F):
+    for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT8, gc.KH4, gc.KI4W, gc.TRUNC2, gc.UNIF2, gc.KH4F):
         gc.run_parity(wl, var, x=x, verbose=False)
 
 

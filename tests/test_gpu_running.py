@@ -82,9 +82,10 @@ def test_ragged(dtype, N, causal):
             gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
 
 
-@pytest.mark.parametrize("N", [1, 5, 64, 100, 200])
-def test_ragged_fp32(N):
-    wl = qin.custom(f"runf32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=True, sigma_qk=1.2, seed=N)
+@pytest.mark.parametrize("N", [1, 5, 64, 100, 200, 257])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_fp32(N, causal):
+    wl = qin.custom(f"runf32_{N}", B=1, H=2, Hkv=1, N=N, d=128, dtype="f32", causal=causal, sigma_qk=1.2, seed=N)
     x = qin.make_inputs(wl)
     for var in (gc.POTR8, gc.POTR4F):
         gc.run_parity(wl, var, x=x, verbose=False)
