@@ -53,6 +53,31 @@ constexpr int KTAB_MAX = 16;  // largest K with a per-row grid table in LDS
 constexpr int BM = NW * 32;   // query rows per workgroup of NW waves
 constexpr int SH = 9;         // log2(BM * 4): the K-interval table's stride between grid values of one row
 
+// Operand reads kept in flight ahead of their MMAs.  A 32-row wave-tile is 36 MMAs of 32 cycles
+// each, every one fed by its own LDS read; issued just before its MMA, each read's full latency
+// sits on the wave's critical path.  The loops below issue the reads RA_K score k-steps and
+// RA_V PV MMAs ahead, and pin that order of LDS reads and MMAs for the scheduler (0: the
+// scheduler's own order).  Measured at 8K, 16K GQA and the GPT-2 shape against the scheduler's
+// order (bit-identical outputs): PoT and exact anchored 2-3.5 % faster, the single pass 1-3 %,
+// the others unchanged; 2 and 2 beat 3 and 2 and 4 and 3.  In the pre-pass (RA_X) 2 ahead
+// gains another 0.5-1.5 % on every anchored kind.  (Accumulators in AGPRs, tried alongside,
+// cost a v_accvgpr_read per score and measured 2-3 % slower at 8K, 8-23 % on the GPT-2 shape.)
+#ifndef QSA_BF16_RA_K
+#define QSA_BF16_RA_K 2
+#endif
+#ifndef QSA_BF16_RA_V
+#define QSA_BF16_RA_V 2
+#endif
+#ifndef QSA_BF16_RA_X
+#define QSA_BF16_RA_X QSA_BF16_RA_K
+#endif
+constexpr int RA_K = QSA_BF16_RA_K;
+constexpr int RA_V = QSA_BF16_RA_V;
+constexpr int RA_X = QSA_BF16_RA_X;  // the same for the K operands of the row-extrema pre-pass
+// Keeps LDS operations and MMAs on their side of this point; VALU, SALU and transcendental
+// instructions may still be scheduled across it.
+__device__ __forceinline__ void pin_lds_mma() { __builtin_amdgcn_sched_barrier(0x0406); }
+
 // Slot of 16-byte chunk q of K row r is q ^ kswz(r): a ds_read_b128 of the score loop reads
 // one chunk of 32 consecutive rows, and the XOR spreads every 16-lane group (and every 8-lane
 // group) over distinct bank groups.
@@ -198,11 +223,24 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
     vtr[db] = (4 * hh + vq) * RR + 16 * ((4 * db + 2 * vg1 + (vp >> 1)) ^ vswz_of<D>(vq)) + 8 * (vp & 1);
 
   // 32-key block kb of the K tile in stage st: init + K_block Q^T  (init: the -M vector, or 0)
+  // The operand of k-step c + RA_K is read while the MMA of k-step c runs (pinned order).
   auto qk1 = [&](int st, int kb, const f32x16& init) __attribute__((always_inline)) {
     const lds_u8* kbase = lds + st * KT + kb * 32 * RR;
     f32x16 s = init;
+    if constexpr (RA_K == 0) {
 #pragma unroll
-    for (int c = 0; c < KC; ++c) s = mma(*(const lds_u32x4*)(kbase + koff[c]), qf[c], c == 0 ? init : s);
+      for (int c = 0; c < KC; ++c) s = mma(*(const lds_u32x4*)(kbase + koff[c]), qf[c], c == 0 ? init : s);
+    } else {
+      u32x4 kr[KC];
+#pragma unroll
+      for (int c = 0; c < RA_K && c < KC; ++c) kr[c] = *(const lds_u32x4*)(kbase + koff[c]);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (c + RA_K < KC) kr[c + RA_K] = *(const lds_u32x4*)(kbase + koff[c + RA_K]);
+        s = mma(kr[c], qf[c], c == 0 ? init : s);
+        pin_lds_mma();
+      }
+    }
     return s;
   };
 
@@ -223,23 +261,37 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
   f32x4 rs = {0.0f, 0.0f, 0.0f, 0.0f};
   u32x4 P[2][2];  // weights of the tile PV multiplies next: [kb][kc]
   // O^T += V^T P^T over the V tile in stage st (two transposing reads per operand), and the row sums
+  // (MMA i = (2 kb + kc) DB + db; the operand of MMA i + RA_V is read while MMA i runs)
   auto pv = [&](int st) __attribute__((always_inline)) {
     const lds_u8* vbase = lds + LY::V0 + st * VT;
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const lds_u8* pa = vbase + (16 * (i / DB)) * RR + vtr[i % DB];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * RR));
+      return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    };
+    constexpr int NV = 4 * DB;  // PV MMAs per tile
+    if constexpr (RA_V == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * RR + vtr[db];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * RR));
-          const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-          o[db] = mma(va, P[kb][kc], o[db]);
-        }
-        rs = mma16(rs_sel, P[kb][kc], rs);
+      for (int i = 0; i < NV; ++i) {
+        const int kb = i / (2 * DB), kc = (i / DB) & 1, db = i % DB;
+        o[db] = mma(vread(i), P[kb][kc], o[db]);
+        if (db == DB - 1) rs = mma16(rs_sel, P[kb][kc], rs);
       }
+    } else {
+      u32x4 va[NV];
+#pragma unroll
+      for (int i = 0; i < RA_V && i < NV; ++i) va[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int kb = i / (2 * DB), kc = (i / DB) & 1, db = i % DB;
+        if (i + RA_V < NV) va[i + RA_V] = vread(i + RA_V);
+        o[db] = mma(va[i], P[kb][kc], o[db]);
+        if (db == DB - 1) rs = mma16(rs_sel, P[kb][kc], rs);
+        pin_lds_mma();
+      }
+    }
   };
 
   // ---- row extrema of the anchored kinds ----------------------------------------------------
@@ -635,15 +687,30 @@ __global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
   for (int c = 0; c < KC; ++c) koff[c] = li * RR + 16 * ((2 * c + hh) ^ kswz_of<D>(li));
   const f32x16 zero16 = {};
   // scores of tile buf for both row blocks: s[rb][kb] = 32 keys kb x 32 rows rb (S^T)
+  // (operand j = KC kb + c; as in fwd_bf16, the operand of j + RA_X is read while j's MMAs run)
   auto qk = [&](int buf, f32x16 (&s)[XRB][2]) {
+    auto kread = [&](int j) __attribute__((always_inline)) {
+      return *(const lds_u32x4*)(lds + buf * KT + (j / KC) * 32 * RR + koff[j % KC]);
+    };
+    if constexpr (RA_X == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const lds_u8* kbase = lds + buf * KT + kb * 32 * RR;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 ka = *(const lds_u32x4*)(kbase + koff[c]);
+      for (int j = 0; j < 2 * KC; ++j) {
+        const int kb = j / KC, c = j % KC;
+        const u32x4 ka = kread(j);
 #pragma unroll
         for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma(ka, qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+      }
+    } else {
+      u32x4 kr[2 * KC];
+#pragma unroll
+      for (int j = 0; j < RA_X; ++j) kr[j] = kread(j);
+#pragma unroll
+      for (int j = 0; j < 2 * KC; ++j) {
+        const int kb = j / KC, c = j % KC;
+        if (j + RA_X < 2 * KC) kr[j + RA_X] = kread(j + RA_X);
+#pragma unroll
+        for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma(kr[j], qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+        pin_lds_mma();
       }
     }
   };
