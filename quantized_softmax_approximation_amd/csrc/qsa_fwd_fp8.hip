@@ -29,6 +29,19 @@
 #include "qsa_mfma_util.h"
 #include "qsa_weights.h"
 
+// Operand read-ahead (A/B switches): QSA_FP8_KRA reads the second score block's K operands of
+// the PoT loop before the weights; QSA_FP8_RAV is the depth of the V operand reads of the
+// interpolating K-interval kinds' bf16 PV product.
+#ifndef QSA_FP8_KRA
+#define QSA_FP8_KRA 1
+#endif
+#ifndef QSA_FP8_RAV
+#define QSA_FP8_RAV 2
+#endif
+#ifndef QSA_FP8_XRA
+#define QSA_FP8_XRA 0
+#endif
+
 namespace qsa {
 namespace {
 
@@ -243,21 +256,52 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
     s[0] = qk1(buf, 0, init);
     s[1] = qk1(buf, 1, init);
   };
+  // the same product split into its operand reads and its MMAs, so that the reads can be
+  // issued well before the MMAs that use them
+  auto kread = [&](int buf, int kb, i32x8 (&ka)[KC]) __attribute__((always_inline)) {
+    const lds_u8* kbase = lds + buf * KT + kb * 32 * KR;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 lo = *(const lds_u32x4*)(kbase + koff[c][0]);
+      const u32x4 hi = *(const lds_u32x4*)(kbase + koff[c][1]);
+      ka[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  };
+  auto kmma = [&](const i32x8 (&ka)[KC], const f32x16& init) __attribute__((always_inline)) {
+    f32x16 s = init;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) s = mma8<0>(ka[c], qf[c], c == 0 ? init : s);
+    return s;
+  };
   // bf16 PV (exact / K-interval): V^T operand via 16-bit transposing reads of the bf16 tile
   const uint32_t vtr16 = (4 * hh + ((lane & 15) >> 2)) * VR + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  // (MMA i = DB kc + db.  For the interpolating K-interval kinds the operand of MMA i + 2 is
+  // read while MMA i runs, in a pinned order: measured 11-12 % faster at 8K.  The exact and
+  // hard-rounding kinds measured 1-3 % slower with it and keep the scheduler's order.)
   auto pv1 = [&](int buf, int kb, const u32x4 (&P)[2], f32x16 (&o)[DB]) {
     const lds_u8* vbase = lds + VB0 + buf * VT + vtr16;
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const lds_u8* pa = vbase + (16 * (2 * kb + i / DB)) * VR + 64 * (i % DB);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * VR));
+      return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    };
+    constexpr int RV = (WK == WK_KI || WK == WK_KI_FLUSH) ? QSA_FP8_RAV : 0, NV = 2 * DB;
+    if constexpr (RV == 0) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+      for (int i = 0; i < NV; ++i) o[i % DB] = mma(vread(i), P[i / DB], o[i % DB]);
+    } else {
+      u32x4 va[NV];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const lds_u8* pa = vbase + (16 * (2 * kb + kc)) * VR + 64 * db;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 8 * VR));
-        const u32x4 va = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-        o[db] = mma(va, P[kc], o[db]);
+      for (int i = 0; i < RV && i < NV; ++i) va[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i + RV < NV) va[i + RV] = vread(i + RV);
+        o[i % DB] = mma(va[i], P[i / DB], o[i % DB]);
+        __builtin_amdgcn_sched_barrier(0x0406);
       }
+    }
   };
   // fp8 PV (PoT): byte e of the P^T operand is key 16(e/8) + 8((e/4)%2) + 4hh + sg(e%4) of the
   // tile, sg = (0, 2, 1, 3) (the byte order in which the weights are packed, see weights8);
@@ -607,6 +651,20 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
       mma_pv8(va, P8c, o);
       read_v8(b1, va);
       prefetch_to(b0, b1);
+#if QSA_FP8_KRA
+      // the second block's K operands are read before the weights, which cover their latency
+      // (measured 1.5-1.9 % faster for PoT at 8K, 1-1.6 % for the single pass)
+      const f32x16 sn0 = qk1(b2, 0, init16);
+      i32x8 k1[KC];
+      kread(b2, 1, k1);
+      __builtin_amdgcn_sched_barrier(0x0406);  // (LDS reads and MMAs stay on their side)
+      prio_lo();
+      if (RUN) run_anchor(s, o, t + 1, false);
+      weights8(s, P8c, t + 1, false);
+      prio_hi();
+      const f32x16 sn1 = kmma(k1, init16);
+      prio_lo();
+#else
       const f32x16 sn0 = qk1(b2, 0, init16);
       prio_lo();
       if (RUN) run_anchor(s, o, t + 1, false);
@@ -614,6 +672,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
       prio_hi();
       const f32x16 sn1 = qk1(b2, 1, init16);
       prio_lo();
+#endif
       s[0] = sn0;
       s[1] = sn1;
       wait_tiles();
@@ -807,17 +866,35 @@ __global__ __launch_bounds__(XNW * 64, XOCC) void rowext_fp8(FwdArgs a) {
     for (int u = 0; u < 2; ++u) koff[c][u] = li * KR + 16 * ((4 * c + 2 * hh + u) ^ kswz_of<D>(li));
   const f32x16 zero16 = {};
   // scores of tile buf for both row blocks: s[rb][kb] = 32 keys kb x 32 rows rb (S^T)
+  // (operand j = KC kb + c; with QSA_FP8_XRA > 0 the operand of j + QSA_FP8_XRA is read while
+  // j's MMAs run, in a pinned order)
   auto qk = [&](int buf, f32x16 (&s)[XRB][2]) {
+    auto kread = [&](int j) __attribute__((always_inline)) {
+      const lds_u8* kbase = lds + buf * KT + (j / KC) * 32 * KR;
+      const u32x4 lo = *(const lds_u32x4*)(kbase + koff[j % KC][0]);
+      const u32x4 hi = *(const lds_u32x4*)(kbase + koff[j % KC][1]);
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    constexpr int RX = QSA_FP8_XRA, NJ = 2 * KC;
+    if constexpr (RX == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const lds_u8* kbase = lds + buf * KT + kb * 32 * KR;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 lo = *(const lds_u32x4*)(kbase + koff[c][0]);
-        const u32x4 hi = *(const lds_u32x4*)(kbase + koff[c][1]);
-        const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      for (int j = 0; j < NJ; ++j) {
+        const int kb = j / KC, c = j % KC;
+        const i32x8 ka = kread(j);
 #pragma unroll
         for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma8<0>(ka, qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+      }
+    } else {
+      i32x8 kr[NJ];
+#pragma unroll
+      for (int j = 0; j < RX && j < NJ; ++j) kr[j] = kread(j);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int kb = j / KC, c = j % KC;
+        if (j + RX < NJ) kr[j + RX] = kread(j + RX);
+#pragma unroll
+        for (int rb = 0; rb < XRB; ++rb) s[rb][kb] = mma8<0>(kr[j], qf[rb][c], c == 0 ? zero16 : s[rb][kb]);
+        __builtin_amdgcn_sched_barrier(0x0406);
       }
     }
   };
