@@ -108,17 +108,17 @@ template <int D> struct Lay {
 // the d = 64 kernels fit without spills), so that the short, latency-bound rows of small heads
 // have three waves per SIMD to interleave; 2 at d = 128 (the O accumulator alone is 64 VGPRs).
 template <int D> constexpr int fwd_occ() { return D == 64 ? 3 : 2; }
-// Waves per workgroup.  At d = 128 the exact, PoT, single-pass and interpolating kinds run 8
-// waves (256 query rows) and one workgroup per CU: the same two waves per SIMD, but each K or V
-// tile is half the load instructions per wave and one LDS copy serves twice the rows, and the
-// kernel fits in fewer registers (216-245 VGPRs against 245-256).  Measured at 8K against 4
-// waves: exact online 3.8 % / 2.4 % faster (non-causal / causal), single-pass PoT 3.3 % / 2.3 %,
-// PoT 1.4 % / 0.7 %, exact anchored 1.8 % / 0.4 %, interpolation 1.7 % / 0.5 %.  Hard rounding
-// and the support kinds measured 0.6-2.5 % slower with 8 and keep 4, as does d = 64, whose
-// register budget is sized for three 4-wave workgroups per CU instead (fwd_occ).
+// Waves per workgroup.  At d = 128 the exact, PoT, single-pass and K-interval kinds run 8 waves
+// (256 query rows) and one workgroup per CU: the same two waves per SIMD, but each K or V tile is
+// half the load instructions per wave and one LDS copy serves twice the rows, and the kernel
+// fits in fewer registers (216-245 VGPRs against 245-256).  Measured at 8K against 4 waves:
+// exact online 3.8 % / 2.4 % faster (non-causal / causal), single-pass PoT 3.3 % / 2.3 %, PoT
+// 1.4 % / 0.7 %, exact anchored 1.8 % / 0.4 %, interpolation 1.7 % / 0.5 %; hard rounding 0.5-2 %
+// once the operand reads ran ahead (before that it measured 0.6-2.5 % slower with 8).  The
+// support kinds keep 4, as does d = 64, whose register budget is sized for three 4-wave
+// workgroups per CU instead (fwd_occ).
 template <int D, int WK> constexpr int fwd_waves() {
-  return (D == 128 && (WK == WK_EXACT || WK == WK_EXACT_ANCH || wk_pot(WK) || WK == WK_KI || WK == WK_KI_FLUSH)) ? 8
-                                                                                                                  : NW;
+  return (D == 128 && (WK == WK_EXACT || WK == WK_EXACT_ANCH || wk_pot(WK) || wk_kint(WK))) ? 8 : NW;
 }
 
 template <int D, int WK, bool DUMP, bool TAB, int NWT = NW>
