@@ -35,9 +35,10 @@
 //     head), the same number of instructions in every wave, issued right after
 //     the iteration's V operand reads (the compiler makes transposing LDS reads
 //     wait for every LDS-direct load issued before them);
-//   * K-interval grid values come from a per-row table of T_l in LDS (K+1
-//     values per row, no transcendental per element; interpolation takes
-//     T_l+1 = T_l e^-Delta) for K <= 16; larger K evaluates T_l = 2^(l step)
+//   * K-interval grid values come from a per-row table in LDS for K <= 16 (no
+//     transcendental per element): T_l for hard rounding, and for
+//     interpolation the line of each interval as a function of the raw score,
+//     so that one FMA gives the weight; larger K evaluates T_l = 2^(l step)
 //     per element.
 #include "qsa_common.h"
 #include "qsa_mfma_util.h"
@@ -303,9 +304,8 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
     M = row < N ? bitsf(park[0]) : 0.0f;
     MN = row < N ? bitsf(park[1]) : 0.0f;
   }
-  RowC rc = make_row<WK, SHK, true>(a, M, MN, wave * 32 + li, TAB ? Tb : nullptr, hh, 2);
-  // interpolation: T_l+1 = T_l e^-Delta = T_l 2^step
-  const float rstep = INTERP && TAB ? __builtin_amdgcn_exp2f(rc.step) - 1.0f : 0.0f;
+  // hard rounding: T_l per row; interpolation: the line (A_l, B_l) of each interval per row
+  RowC rc = make_row<WK, SHK, INTERP ? TAB_SLOPE : TAB_T>(a, M, MN, wave * 32 + li, TAB ? Tb : nullptr, hh, 2);
   // main-loop score accumulators start at -M: s' = acc - M
   f32x16 init;
 #pragma unroll
@@ -444,23 +444,34 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
             i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
             i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
           }
-        } else {  // K-interval, interpolation between T_l and T_l+1, l = floor(min(y, K))
+        } else if (TAB) {  // K-interval, interpolation between T_l and T_l+1, l = floor(min(y, K))
+          // t = y + 2^23 - 1/2 rounded by the FMA: for y >= 1/2 the low bits of t hold floor(y)
+          // (at an integer y either neighbour, where the weight is continuous); one v_med3_f32
+          // clamps t to [2^23, 2^23 + K], whose floats order as their bit patterns, so
+          // bits(t) - 0x4B000000 = l in [0, K].  The table's line of interval l then gives the
+          // weight from the raw score in one FMA (flushing kind: entry K is 0).
+          const float t0 = fmaf(x0, -rc.c, 8388607.5f), t1 = fmaf(x1, -rc.c, 8388607.5f);
+          const uint32_t b0 = fbits(__builtin_amdgcn_fmed3f(t0, 8388608.0f, kt_hi));
+          const uint32_t b1 = fbits(__builtin_amdgcn_fmed3f(t1, 8388608.0f, kt_hi));
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          // (b << (SHK + 1)) drops 0x4B000000: the table's stride is 2^(SHK+1) bytes per l
+          const f2 e0 = *(const f2*)(Tb + ((b0 << (SHK + 1)) + rc.tab));
+          const f2 e1 = *(const f2*)(Tb + ((b1 << (SHK + 1)) + rc.tab));
+          pk = pack_bf16(fmaf(x0, e0.y, e0.x), fmaf(x1, e1.y, e1.x));
+          if (DUMP) {
+            const uint32_t l0 = b0 - 0x4B000000u, l1 = b1 - 0x4B000000u;
+            i0 = (FLUSH && l0 == (uint32_t)a.levels) ? 254u : l0;
+            i1 = (FLUSH && l1 == (uint32_t)a.levels) ? 254u : l1;
+          }
+        } else {  // interpolation for K > 16: T_l and T_l+1 evaluated per element
           const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
           const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
           const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
           const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
-          float w0, w1;
-          if (TAB) {  // T_l (1 + t (e^-Delta - 1)); at l = K the parameter t is 0
-            const float T0 = *(const float*)(Tb + ((l0 << SHK) + rc.tab));
-            const float T1 = *(const float*)(Tb + ((l1 << SHK) + rc.tab));
-            w0 = T0 * fmaf(c0 - f0, rstep, 1.0f);
-            w1 = T1 * fmaf(c1 - f1, rstep, 1.0f);
-          } else {
-            typedef float f2 __attribute__((ext_vector_type(2)));
-            const f2 e0 = kgrid_pair(rc.step, f0), e1 = kgrid_pair(rc.step, f1);  // (T_l, T_l+1 - T_l)
-            w0 = fmaf(c0 - f0, e0.y, e0.x);
-            w1 = fmaf(c1 - f1, e1.y, e1.x);
-          }
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          const f2 e0 = kgrid_pair(rc.step, f0), e1 = kgrid_pair(rc.step, f1);  // (T_l, T_l+1 - T_l)
+          float w0 = fmaf(c0 - f0, e0.y, e0.x);
+          float w1 = fmaf(c1 - f1, e1.y, e1.x);
           if (FLUSH) {
             w0 = y0 > Kf ? 0.0f : w0;
             w1 = y1 > Kf ? 0.0f : w1;
@@ -815,8 +826,8 @@ __global__ __launch_bounds__(XNW * 64, 2) void rowext_bf16(FwdArgs a) {
 template <int D, int WK, bool TAB>
 hipError_t launch_main(const FwdArgs& a, hipStream_t st) {
   constexpr int NWK = fwd_waves<D, WK>();
-  // the table holds T_l alone for both hard rounding and interpolation
-  const size_t lds = (size_t)Lay<D>::TAB + (TAB ? (size_t)(NWK * 32) * (a.levels + 1) * 4 : 0);
+  // hard rounding: T_l (4 bytes a row and level); interpolation: the interval lines (8 bytes)
+  const size_t lds = (size_t)Lay<D>::TAB + (TAB ? table_bytes(WK, NWK * 32, a.levels) : 0);
   FwdArgs g = a;  // query tiles of NWK * 32 rows
   g.n_qtiles = (a.N + NWK * 32 - 1) / (NWK * 32);
   g.total_blocks = a.B * a.H * g.n_qtiles;

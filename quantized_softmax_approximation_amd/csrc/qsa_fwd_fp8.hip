@@ -360,7 +360,8 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
     MN = row < N ? bitsf(park[1]) : 0.0f;
   }
 
-  RowC rc = make_row<WK, SHK>(a, M, MN, wave * 32 + li, Tb, hh, 2);
+  // interpolation: the line (A_l, B_l) of each interval per row, as in the bf16 kernel
+  RowC rc = make_row<WK, SHK, (WK == WK_KI || WK == WK_KI_FLUSH) ? TAB_SLOPE : TAB_PAIRS>(a, M, MN, wave * 32 + li, Tb, hh, 2);
   f32x16 init16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) init16[r] = ANCH ? -M : 0.0f;
@@ -454,23 +455,22 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void fwd_fp8(FwdArgs a) {
             i0 = (FLUSH && y0 > Kf) ? 254u : (uint32_t)(b0 - 0x4B000000);
             i1 = (FLUSH && y1 > Kf) ? 254u : (uint32_t)(b1 - 0x4B000000);
           }
-        } else {  // K-interval, interpolation
-          const float y0 = -x0 * rc.c, y1 = -x1 * rc.c;
-          const float c0 = __builtin_amdgcn_fmed3f(y0, 0.0f, Kf), c1 = __builtin_amdgcn_fmed3f(y1, 0.0f, Kf);
-          const float f0 = __builtin_floorf(c0), f1 = __builtin_floorf(c1);
-          const uint32_t l0 = (uint32_t)(int32_t)f0, l1 = (uint32_t)(int32_t)f1;
+        } else {  // K-interval, interpolation between T_l and T_l+1, l = floor(min(y, K))
+          // t = y + 2^23 - 1/2 rounded by the FMA holds floor(y) in its low bits for y >= 1/2 (at
+          // an integer y either neighbour, where the weight is continuous); the v_med3_f32
+          // clamps l to [0, K]; the table's line of interval l gives the weight from the raw
+          // score in one FMA (flushing kind: entry K is 0)
+          const float t0 = fmaf(x0, -rc.c, 8388607.5f), t1 = fmaf(x1, -rc.c, 8388607.5f);
+          const uint32_t b0 = fbits(__builtin_amdgcn_fmed3f(t0, 8388608.0f, kt_hi));
+          const uint32_t b1 = fbits(__builtin_amdgcn_fmed3f(t1, 8388608.0f, kt_hi));
           typedef float f2 __attribute__((ext_vector_type(2)));
-          const f2 e0 = *(const f2*)(Tb + ((l0 << (SHK + 1)) + rc.tab));
-          const f2 e1 = *(const f2*)(Tb + ((l1 << (SHK + 1)) + rc.tab));
-          float w0 = fmaf(c0 - f0, e0.y, e0.x), w1 = fmaf(c1 - f1, e1.y, e1.x);
-          if (FLUSH) {
-            w0 = y0 > Kf ? 0.0f : w0;
-            w1 = y1 > Kf ? 0.0f : w1;
-          }
-          pk = pack_bf16(w0, w1);
+          const f2 e0 = *(const f2*)(Tb + ((b0 << (SHK + 1)) + rc.tab));
+          const f2 e1 = *(const f2*)(Tb + ((b1 << (SHK + 1)) + rc.tab));
+          pk = pack_bf16(fmaf(x0, e0.y, e0.x), fmaf(x1, e1.y, e1.x));
           if (DUMP) {
-            i0 = (FLUSH && y0 > Kf) ? 254u : l0;
-            i1 = (FLUSH && y1 > Kf) ? 254u : l1;
+            const uint32_t l0 = b0 - 0x4B000000u, l1 = b1 - 0x4B000000u;
+            i0 = (FLUSH && l0 == (uint32_t)L) ? 254u : l0;
+            i1 = (FLUSH && l1 == (uint32_t)L) ? 254u : l1;
           }
         }
         const int k0 = kt * BN + kb * 32 + acc_key(r0, hh);

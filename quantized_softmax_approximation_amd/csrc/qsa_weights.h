@@ -169,10 +169,17 @@ template <> struct Weight<WK_UNIF> : SupportW<true> {};
 // the weights then evaluate T_l = 2^(l step) from the index with the same
 // instruction, which gives the same values without the table).  The K+1
 // table entries are split between the `nsplit` lanes that share a row (this
-// lane writes entries part, part + nsplit, ...).  TONLY: the interpolation
-// table holds T_l alone, like the hard-rounding one (the kernel forms T_l+1
-// from T_l), instead of the pairs (T_l, T_l+1 - T_l).
-template <int WK, int SH, bool TONLY = false>
+// lane writes entries part, part + nsplit, ...).  TMODE picks the layout of
+// the interpolation table (the hard-rounding table is T_l alone in every mode):
+//   TAB_PAIRS  (T_l, T_l+1 - T_l), 8 bytes per entry;
+//   TAB_T      T_l alone (the kernel forms T_l+1 from T_l);
+//   TAB_SLOPE  the line of interval l as a function of the raw score difference
+//              x = s - m (y = -c x): (A_l, B_l) with A_l = T_l - l (T_l+1 - T_l) and
+//              B_l = -c (T_l+1 - T_l), so that the weight on [l, l+1] is
+//              A_l + B_l x = T_l + (y - l)(T_l+1 - T_l); entry K is (T_K, 0), or
+//              (0, 0) for the flushing kind, whose weight is 0 once floor(y) >= K.
+enum : int { TAB_PAIRS = 0, TAB_T = 1, TAB_SLOPE = 2 };
+template <int WK, int SH, int TMODE = TAB_PAIRS>
 __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, int row_local,
                                          unsigned char* tab, int part, int nsplit) {
   RowC rc;
@@ -197,7 +204,7 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
   rc.mc = M * rc.c;
   const float step = -delta_s * kLog2e;
   rc.step = step;
-  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH) && !TONLY;
+  constexpr bool INTERP = (WK == WK_KI || WK == WK_KI_FLUSH) && TMODE != TAB_T;
   constexpr int ROWS = (1 << SH) / 4;
   rc.tab = (uint32_t)row_local * (INTERP ? 8u : 4u);
   if (tab == nullptr) return rc;
@@ -206,7 +213,12 @@ __device__ __forceinline__ RowC make_row(const FwdArgs& a, float M, float MN, in
     if (INTERP) {
       const float t1 = (l < K) ? __builtin_amdgcn_exp2f(step * (float)(l + 1)) : t0;
       typedef float f2 __attribute__((ext_vector_type(2)));
-      *(f2*)(tab + ((size_t)l * ROWS + row_local) * 8) = f2{t0, t1 - t0};
+      f2 e = {t0, t1 - t0};
+      if (TMODE == TAB_SLOPE) {
+        e = f2{fmaf(-(float)l, e.y, t0), -rc.c * e.y};
+        if (WK == WK_KI_FLUSH && l == K) e = f2{0.0f, 0.0f};
+      }
+      *(f2*)(tab + ((size_t)l * ROWS + row_local) * 8) = e;
     } else {
       *(float*)(tab + ((size_t)l * ROWS + row_local) * 4) = t0;
     }
