@@ -56,6 +56,22 @@ def test_gpt2(gpt2, var):
     gc.run_parity(wl, var, heads=heads, x=x, dev_t=dev_t, f64=f64)
 
 
+@pytest.fixture(scope="module")
+def gpt2_wide():
+    # d = 64 on a grid large enough for the pre-pass with two 32-row blocks per wave
+    # (B H N/256 >= 512; the GPT-2 shape runs one block per wave)
+    wl = qin.custom("gpt2_wide", B=2, H=64, Hkv=64, N=1024, d=64, dtype="bf16", causal=True, sigma_qk=1.5, seed=1012)
+    x = qin.make_inputs(wl)
+    return wl, x, gc.to_gpu(x), gc.decoded(x)
+
+
+@pytest.mark.parametrize("var", [gc.EXACT_ANCH, gc.POT8, gc.KH4, gc.KI4, gc.KI16W, gc.KH4F, gc.TRUNC2], ids=gc.name)
+def test_gpt2_wide_prepass(gpt2_wide, var):
+    wl, x, dev_t, f64 = gpt2_wide
+    gc.run_parity(wl, var, heads=[(0, 0), (1, 63)], windows=gc.sample_windows(wl.N, n=3, seed=21), x=x,
+                  dev_t=dev_t, f64=f64)
+
+
 # ---------------------------------------------------------------- 2K with attention sink (bf16, d=128)
 
 @pytest.fixture(scope="module")
