@@ -103,8 +103,9 @@ def run_parity(wl, var, *, windows=None, heads=None, tol=None, x=None, dev_t=Non
     qf, kf, vf = f64 if f64 is not None else decoded(x)
     B, H, N, d = x.q.shape
     group = H // x.k.shape[1]
+    fp8 = x.q.dtype == torch.float8_e4m3fn
     if tol is None:
-        tol = 3e-2 if x.q.dtype == torch.float8_e4m3fn else 1e-2
+        tol = 3e-2 if fp8 else 1e-2
     windows = windows or [(0, N)]
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
     ovar = oracle_var(var)
@@ -124,11 +125,11 @@ def run_parity(wl, var, *, windows=None, heads=None, tol=None, x=None, dev_t=Non
         for (b, h) in heads:
             kvh = h // group
             r, _ = parity.compare_head(ovar, qf[b, h], kf[b, kvh], vf[b, kvh], rows, o_np[b, h, r0:r0 + nr],
-                                       None if g_np is None else g_np[b, h], causal=wl.causal, tol=tol)
+                                       None if g_np is None else g_np[b, h], causal=wl.causal, tol=tol, fp8=fp8)
             rep.merge(r)
             if o_plain is not None:
                 parity.compare_head(ovar, qf[b, h], kf[b, kvh], vf[b, kvh], rows, o_plain[b, h, r0:r0 + nr], None,
-                                    causal=wl.causal, tol=tol)
+                                    causal=wl.causal, tol=tol, fp8=fp8)
         rep.plain_differs += int(o_plain is not None)
     if verbose:
         print(f"[parity] {name(var)}: rows={rep.rows} agree={rep.idx_agree:.6f} disagree={rep.idx_disagree} "

@@ -304,3 +304,61 @@ def test_fp8_ragged(N, d, causal):
     for var in (gc.EXACT, gc.EXACT_ANCH, gc.POT16, gc.POT4F, gc.KH4, gc.KI16, gc.KH4WF, gc.KI4WF, gc.TRUNC2,
                 gc.UNIF2, gc.KH4F):
         gc.run_parity(wl, var, x=x, dev_t=dev_t, f64=f64, verbose=False)
+
+
+# ---------------------------------------------------------------- the score-error model of the protocol
+
+@pytest.mark.parametrize("dtype,d,sigma", [("fp8", 64, 1.0), ("fp8", 128, 1.5), ("fp8", 128, 4.0), ("bf16", 64, 1.5),
+                                           ("bf16", 128, 1.5)])
+def test_score_error_within_band(dtype, d, sigma):
+    # the band of the parity protocol rests on a bound of the score error: fp32 accumulation for
+    # bf16 inputs, GAMMA_FP8 for the 8-bit MFMA.  The row maxima (the largest score of each row,
+    # as the kernel's MMAs computed it) against exact float64 check that bound on every row.
+    import oracle
+    wl = qin.custom(f"err_{dtype}{d}", B=1, H=4, N=1024, d=d, dtype=dtype, causal=False, sigma_qk=sigma,
+                    seed=40 + d + int(4 * sigma))
+    x = qin.make_inputs(wl)
+    dev_t = gc.to_gpu(x)
+    qf, kf, vf = gc.decoded(x)
+    _, _, st = gc.gpu_call(x, dev_t, gc.EXACT_ANCH, causal=False, stats=True)
+    sc = 1.0 / np.sqrt(d)
+    for h in range(4):
+        m_gpu = st["row_max"][0, h].cpu().numpy().astype(np.float64)
+        m = (sc * (qf[0, h] @ kf[0, h].T)).max(1)
+        A = sc * np.max(np.abs(qf[0, h]) @ np.abs(kf[0, h]).T, axis=1)
+        gamma = parity.score_gamma(d, fp8=dtype == "fp8")
+        # (+ the rounding of the exported m = M * scale, one fp32 product)
+        assert np.all(np.abs(m_gpu - m) <= gamma * A + 2 * parity.U * np.abs(m))
+
+
+# ---------------------------------------------------------------- seeded random configurations
+
+def _random_cases(n, seed):
+    r = np.random.default_rng(seed)
+    for i in range(n):
+        dtype = r.choice(["bf16", "bf16", "fp8"])
+        kind = r.choice(["ki", "ki", "kh", "pot", "potr"])
+        if kind == "pot":
+            var = dict(kind="pot", levels=int(r.choice([2, 8, 16])), flush=bool(r.random() < 0.3))
+        elif kind == "potr":
+            var = dict(kind="pot_running", levels=int(r.choice([2, 8, 16])), flush=bool(r.random() < 0.3))
+        else:
+            var = dict(kind="kint", levels=int(r.choice([1, 2, 4, 7, 16])), interp=bool(kind == "ki"))
+            win = r.choice([0.0, 0.0, 2.0, 8.0])
+            if win:
+                var["window"] = float(win)
+                if r.random() < 0.4:
+                    var["flush"] = True
+        wl = qin.custom(f"rnd{i}", B=1, H=int(r.choice([1, 2, 4])), N=int(r.choice([33, 127, 200, 257, 511, 640])),
+                        d=int(r.choice([64, 128])), dtype=str(dtype), causal=bool(r.random() < 0.6),
+                        sigma_qk=float(r.choice([0.5, 1.0, 1.5, 2.5, 4.0])), seed=int(r.integers(1 << 20)))
+        yield wl, var
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_configurations(block):
+    # sizes, scales, dtypes, head dimensions and K-interval / PoT parameters drawn at random
+    # (seeded), away from the fixed workloads: the interpolation lines, the clamps of the grid
+    # coordinate and the single-pass anchors on inputs no other case uses
+    for wl, var in _random_cases(25, seed=500 + block):
+        gc.run_parity(wl, var, verbose=False)

@@ -125,12 +125,13 @@ def test_row_stats_are_the_final_anchor_and_sum(dtype):
             # the anchor is an integer: the definition's, or, where a tile maximum is within the
             # fp32 band of an integer, the final anchor of another sequence fp32 may produce
             np.testing.assert_allclose(A, np.rint(A), atol=1e-4)
-            cands = parity.anchor_candidates(var, qf[0, h], kf[0, h], np.arange(257), causal=True)
+            cands = parity.anchor_candidates(var, qf[0, h], kf[0, h], np.arange(257), causal=True,
+                                             fp8=dtype == "fp8")
             assert all(np.rint(A[i]) in {c[-1] for c in cands[i]} for i in range(257))
             assert np.mean(np.rint(A) == ref["A"]) >= 0.99
             parity.compare_head(var, qf[0, h], kf[0, h], vf[0, h], np.arange(257), o[0, h].float().cpu().numpy(),
                                 causal=True, tol=3e-2 if dtype == "fp8" else 1e-2,
-                                l_gpu=st["row_sum"][0, h].cpu().numpy())
+                                l_gpu=st["row_sum"][0, h].cpu().numpy(), fp8=dtype == "fp8")
 
 
 def test_deterministic_and_no_row_lo():

@@ -145,6 +145,26 @@ def test_wrong_index_outside_band_fails():
         parity.compare_head(var, q, k, v, np.arange(N), O2, idx, causal=False, tol=1e-2)
 
 
+def test_fp8_band_still_catches_a_wrong_index():
+    # the 8-bit MFMA's band (gamma 2^-12) is still far narrower than the distance of a
+    # planted flip from its edge
+    r = np.random.default_rng(9)
+    N, d = 128, 64
+    q, k, v = r.standard_normal((N, d)) * 1.5, r.standard_normal((N, d)) * 1.5, r.standard_normal((N, d))
+    var = dict(kind="pot", levels=8)
+    O, idx = emulate(var, q, k, v, False)
+    rep, ref = parity.compare_head(var, q, k, v, np.arange(N), O, idx, causal=False, tol=1e-4, fp8=True)
+    assert rep.idx_bad == 0 and rep.idx_agree >= 0.999
+    y = ref["y"]
+    far = (np.abs(y - np.floor(y) - 0.5) > 0.25) & (idx < 7)
+    i, j = np.argwhere(far)[0]
+    bad = idx.copy()
+    bad[i, j] += 1
+    with pytest.raises(AssertionError):
+        parity.compare_head(var, q, k, v, np.arange(N), O, bad, causal=False, tol=1e-4, fp8=True)
+    assert parity.score_gamma(64, fp8=True) == 2.0 ** -12 and parity.score_gamma(64) == 128 * 2.0 ** -24
+
+
 def _on_integer_anchor(N=150, d=64, row=100, key=10, n=3, seed=8):
     """Inputs whose row `row` has its largest score of key tile 0 at key `key`, equal to
     n ln 2 up to float64 rounding: that tile's anchor is n or n + 1 in fp32."""
