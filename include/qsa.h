@@ -197,9 +197,11 @@ typedef struct {
                                /*   final running maximum; QSA_POT_RUNNING: to the final */
                                /*   anchor).                                             */
   unsigned char* grid_idx;     /* [B,H,idx_rows,N] u8: per element the grid index l (K-  */
-                               /*   interval; interpolation: floor(y) clipped to K) or   */
-                               /*   the exponent e (PoT); 0 for exact kinds and for the  */
-                               /*   kept keys of QSA_TRUNC / QSA_UNIFORM;                */
+                               /*   interval; interpolation: floor(y) clipped to K; at   */
+                               /*   an integer y either neighbour, where the weight is   */
+                               /*   the same) or the exponent e (PoT); 0 for exact       */
+                               /*   kinds and for the kept keys of QSA_TRUNC /           */
+                               /*   QSA_UNIFORM;                                         */
                                /*   QSA_IDX_FLUSHED (also: outside the support) /        */
                                /*   QSA_IDX_MASKED otherwise.                            */
   int idx_row0;                /* first query row dumped into grid_idx                   */
