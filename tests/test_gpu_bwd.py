@@ -197,6 +197,25 @@ def test_bwd_pot2k_sampled(var, grad):
     _case(wl, var, grad, heads=[(0, 0), (wl.B - 1, wl.H - 1)])
 
 
+def _random_bwd_cases(n, seed):
+    r = np.random.default_rng(seed)
+    for i in range(n):
+        hkv = int(r.choice([1, 2]))
+        wl = qin.custom(f"bwd_rnd{i}", B=int(r.choice([1, 2])), H=hkv * int(r.choice([1, 2, 4])), Hkv=hkv,
+                        N=int(r.choice([17, 64, 100, 129, 200, 257])), d=int(r.choice([64, 128])),
+                        dtype=str(r.choice(["bf16", "bf16", "f32"])), causal=bool(r.random() < 0.6),
+                        sigma_qk=float(r.choice([0.7, 1.2, 1.5, 2.5])), seed=int(r.integers(1 << 20)))
+        yield wl, KINDS[int(r.integers(len(KINDS)))], MODES[int(r.integers(len(MODES)))]
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_bwd_random_configurations(block):
+    # shapes, grouped heads, masks, score scales, weight kinds and gradient modes drawn at random
+    # (seeded), away from the fixed cases above
+    for wl, var, grad in _random_bwd_cases(30, seed=700 + block):
+        _case(wl, var, grad)
+
+
 def test_bwd_rejects_fp8():
     x = qin.make_inputs(qin.custom("bwd_fp8", N=64, dtype="fp8"))
     q, k, v = (t.cuda() for t in (x.q, x.k, x.v))
