@@ -362,3 +362,40 @@ def test_random_configurations(block):
     # coordinate and the single-pass anchors on inputs no other case uses
     for wl, var in _random_cases(25, seed=500 + block):
         gc.run_parity(wl, var, verbose=False)
+
+
+def _random_wide_cases(n, seed):
+    r = np.random.default_rng(seed)
+    for i in range(n):
+        dtype = str(r.choice(["bf16", "bf16", "fp8", "fp8", "f32"]))
+        kind = str(r.choice(["ki", "kh", "pot", "potr", "exact", "exact_anchored", "trunc", "uniform"]))
+        top = 16 if dtype == "fp8" else 64
+        if kind == "pot":
+            var = dict(kind="pot", levels=min(top, int(r.choice([1, 2, 3, 8, 16, 32]))), flush=bool(r.random() < 0.3))
+        elif kind == "potr":
+            var = dict(kind="pot_running", levels=int(r.choice([2, 5, 8, 16])), flush=bool(r.random() < 0.3))
+        elif kind in ("exact", "exact_anchored"):
+            var = dict(kind=kind)
+        elif kind in ("trunc", "uniform"):
+            var = dict(kind=kind, window=float(r.choice([0.5, 2.0, 8.0])))
+        else:
+            var = dict(kind="kint", levels=min(top, int(r.choice([1, 2, 3, 4, 8, 16, 31]))), interp=kind == "ki")
+            win = float(r.choice([0.0, 0.0, 1.0, 4.0, 8.0]))
+            if win:
+                var["window"] = win
+            if r.random() < 0.3:
+                var["flush"] = True
+        hkv = int(r.choice([1, 2]))
+        wl = qin.custom(f"wide{i}", B=int(r.choice([1, 2, 3])), H=hkv * int(r.choice([1, 2, 4, 8])), Hkv=hkv,
+                        N=int(r.choice([1, 2, 31, 64, 65, 129, 200, 383, 520])), d=int(r.choice([64, 128])),
+                        dtype=dtype, causal=bool(r.random() < 0.5), sigma_qk=float(r.choice([0.5, 1.0, 1.5, 2.5, 4.0])),
+                        seed=int(r.integers(1 << 20)), sink=bool(r.random() < 0.2))
+        yield wl, var
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_random_configurations_wide(block):
+    # every kind and dtype, batch > 1, grouped key/value heads, the attention-sink key, and sizes
+    # down to a single key, drawn at random (seeded)
+    for wl, var in _random_wide_cases(50, seed=900 + block):
+        gc.run_parity(wl, var, verbose=False)

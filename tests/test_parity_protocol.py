@@ -196,3 +196,30 @@ def test_single_pass_wrong_anchor_fails():
     O2, idx2 = emulate(var, q, k, v, False, anchor_override=[(7, 0, A0 + 1)])
     with pytest.raises(AssertionError):
         parity.compare_head(var, q, k, v, np.arange(150), O2, idx2, causal=False, tol=1e-4)
+
+
+def test_agreement_floor_allows_one_element_in_a_small_head():
+    # 20 x 20 visible elements (below the 1000 at which 0.1 % is one element): rows 0 and 1 each
+    # get a key on the PoT edge y = 1/2 (inside the band), where both indices are correct.  One
+    # flipped there passes; two fail the floor, although each lies in the band.
+    r = np.random.default_rng(11)
+    N, d = 20, 64
+    q, k, v = r.standard_normal((N, d)), r.standard_normal((N, d)), r.standard_normal((N, d))
+    sc = 1.0 / math.sqrt(d)
+    for i, j in ((0, 5), (1, 6)):
+        s = sc * (q[i] @ k.T)
+        m = np.max(np.delete(s, j))
+        t = m - 0.5 * math.log(2.0)                    # the score that puts key j on y = 1/2
+        k[j] += (t - s[j]) / (sc * (q[i] @ q[i])) * q[i]
+    var = dict(kind="pot", levels=8)
+    O, _ = emulate(var, q, k, v, False)
+    _, ref = parity.compare_head(var, q, k, v, np.arange(N), O, None, causal=False, tol=1e-4)
+    assert abs(ref["y"][0, 5] - 0.5) < 1e-12 and abs(ref["y"][1, 6] - 0.5) < 1e-12
+    one = ref["idx"].astype(np.uint8)                  # the oracle's choices at both ties ...
+    one[0, 5] ^= 1                                      # ... and the other one at (0, 5)
+    rep, _ = parity.compare_head(var, q, k, v, np.arange(N), O, one, causal=False, tol=1e-4)
+    assert rep.idx_disagree == 1 and rep.idx_bad == 0
+    two = one.copy()
+    two[1, 6] ^= 1
+    with pytest.raises(AssertionError, match="index agreement"):
+        parity.compare_head(var, q, k, v, np.arange(N), O, two, causal=False, tol=1e-4)
