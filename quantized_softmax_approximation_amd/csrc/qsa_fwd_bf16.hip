@@ -330,6 +330,14 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
   float A = -__builtin_inff(), Aw = -__builtin_inff();
   int dlag = 0;
   float tb = pot_g;
+  // pre-pass PoT without flush at d = 64: t = 1 - ((L-1) - y) 2^-24 from one FMA whose output
+  // clamp is the clip (pot_t_clamped), one VALU instruction per element fewer than the integer
+  // max.  Measured 2.7 % faster per call at d = 64 (GPT-2 shape) and 0.6-0.8 % slower at
+  // d = 128, where the integer max stays.
+  constexpr bool POT_CLAMP = POT && !FLUSH && !RUN && D == 64;
+  const float pot_nc = -rc.c * 5.9604644775390625e-8f;                  // -c 2^-24
+  const float pot_b = 1.0f - (float)(L - 1) * 5.9604644775390625e-8f;   // 1 - (L-1) 2^-24
+  const uint32_t pot_kadd = 0x00010001u * (uint32_t)((128 - L) << 7);
 
   // scale the row sums by each row's factor (held by the lane of that row)
   auto rs_scale = [&](float alpha) { rs *= bitsf(__builtin_amdgcn_ds_bpermute(4 * rs_q, (int)fbits(alpha))); };
@@ -399,6 +407,12 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
           if (DUMP) {
             i0 = y0 > rc.cut ? 254u : 0u;
             i1 = y1 > rc.cut ? 254u : 0u;
+          }
+        } else if (POT_CLAMP) {
+          pk = pot_pair_k(pot_t_clamped(x0, pot_nc, pot_b), pot_t_clamped(x1, pot_nc, pot_b), pot_kadd);
+          if (DUMP) {
+            i0 = 127u - ((pk >> 7) & 0x1FFu);
+            i1 = 127u - ((pk >> 23) & 0x1FFu);
           }
         } else if (POT && !FLUSH) {
           // t = G + (acc - M) c = G - y, rounded to an integer by the FMA itself

@@ -88,4 +88,22 @@ __device__ __forceinline__ uint32_t pot_pair(float t0, float t1, int32_t lo) {
   return w;
 }
 
+// The same pair from t = 1 - k 2^-24 in [1/2, 1], k = (L-1) - e: the FMA that forms t with
+// its output clamp to [0, 1] (v_fma_f32 ... clamp) has already clipped e to L-1 (k >= 0), and
+// bits(t) = 0x3F800000 - k, so the low halves are -k as int16.  (-k)(-128) + (128 - L) 128 =
+// (127 - e) 128 in each half; add holds (128 - L) 128 twice.
+__device__ __forceinline__ uint32_t pot_pair_k(float t0, float t1, uint32_t add) {
+  const uint32_t nk = __builtin_amdgcn_perm(fbits(t1), fbits(t0), 0x05040100u);
+  uint32_t w;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(w) : "v"(nk), "v"(0xFF80FF80u), "v"(add));
+  return w;
+}
+
+// t = 1 - ((L-1) - y) 2^-24 for y = -x c, rounded once and clamped to [0, 1] by one FMA: the
+// rounding takes k = (L-1) - y to an integer (the ulp of [1/2, 1) is 2^-24) and the clamp at 1
+// is the clip y <= L-1.  nc = -c 2^-24 and b = 1 - (L-1) 2^-24 are exact.
+__device__ __forceinline__ float pot_t_clamped(float x, float nc, float b) {
+  return __builtin_amdgcn_fmed3f(fmaf(x, nc, b), 0.0f, 1.0f);
+}
+
 }  // namespace qsa
