@@ -335,6 +335,12 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
   // max.  Measured 2.7 % faster per call at d = 64 (GPT-2 shape) and 0.6-0.8 % slower at
   // d = 128, where the integer max stays.
   constexpr bool POT_CLAMP = POT && !FLUSH && !RUN && D == 64;
+  // With flush the clamp sits at L (pot_bf = 1 - L 2^-24): k = L - e, and k = 0 is the flushed
+  // level.  The low half of bits(t) is then -k: 0 for the flushed level, at least 2^16 - 64
+  // otherwise, so min_u16((-k)(-128) + (127 - L) 128, -k) is the weight (127 - e) << 7, or 0.
+  constexpr bool POT_CLAMP_FLUSH = POT && FLUSH && !RUN;
+  const float pot_bf = 1.0f - (float)L * 5.9604644775390625e-8f;        // 1 - L 2^-24
+  const uint32_t pot_kaddf = 0x00010001u * (uint32_t)((127 - L) << 7);
   const float pot_nc = -rc.c * 5.9604644775390625e-8f;                  // -c 2^-24
   const float pot_b = 1.0f - (float)(L - 1) * 5.9604644775390625e-8f;   // 1 - (L-1) 2^-24
   const uint32_t pot_kadd = 0x00010001u * (uint32_t)((128 - L) << 7);
@@ -421,6 +427,17 @@ __global__ __launch_bounds__(NWT * 64, NWT == 8 ? 1 : fwd_occ<D>()) void fwd_bf1
           if (DUMP) {
             i0 = 127u - ((pk >> 7) & 0x1FFu) + (uint32_t)dlag;  // against the running anchor
             i1 = 127u - ((pk >> 23) & 0x1FFu) + (uint32_t)dlag;
+          }
+        } else if (POT_CLAMP_FLUSH) {
+          const uint32_t nk = __builtin_amdgcn_perm(fbits(pot_t_clamped(x1, pot_nc, pot_bf)),
+                                                    fbits(pot_t_clamped(x0, pot_nc, pot_bf)), 0x05040100u);
+          uint32_t w;
+          asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(w) : "v"(nk), "v"(0xFF80FF80u), "v"(pot_kaddf));
+          pk = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w),
+                                                                      __builtin_bit_cast(u16x2, nk)));
+          if (DUMP) {  // e = L - k; k = 0 is flushed
+            i0 = (nk & 0xFFFFu) == 0 ? 254u : (uint32_t)L - (0x10000u - (nk & 0xFFFFu));
+            i1 = (nk >> 16) == 0 ? 254u : (uint32_t)L - (0x10000u - (nk >> 16));
           }
         } else if (POT) {  // flush: e >= L -> 0
           const float t0 = fmaf(x0, rc.c, tb), t1 = fmaf(x1, rc.c, tb);
